@@ -1,0 +1,189 @@
+"""CPU oracle for the packed ternary GEMV path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or run
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it, to check the HIP kernels and to
+time a plain CPU baseline. It shares no code, header, table or constant
+generator with the HIP library, and it imports nothing from it.
+
+What it computes (Neutrino-1 8B model page, English text on bittide):
+
+* Every transformer linear is stored as ternary codes c in {-1, 0, +1} with a
+  scale and a row sum per row, and the codes are decoded inside the matrix
+  kernels (introduction; "Where the bytes live"; "Inside the coded lane").
+  The page calls the encoding proprietary and never specifies it, so the bit
+  layout below is this project's own (2 bits per code, 16 codes per uint32).
+  Its definition is stated here in words, once, and nowhere else in Python.
+* A linear applied to one activation row x is y_r = s_r * sum_j c_rj * x_j.
+* The untied output head is an int8 tensor with one scale per row
+  ("Where the bytes live"): y_v = s_v * sum_j w_vj * x_j.
+* The speculative verify pass scores a whole drafted run in one forward pass
+  ("speculative" section), i.e. the same products for M activation rows.
+
+Bit layout of one 32-bit word (little-endian uint32) holding 16 codes:
+  code j (0..15) belongs to pair t = j // 2 and half h = j % 2;
+  its NONZERO bit is bit (10 + 16*h + 2*t) mod 32,
+  its SIGN bit    is bit (15 + 16*h + 2*t) mod 32;
+  +1 -> nonzero=1, sign=0;  -1 -> nonzero=1, sign=1;  0 -> both bits 0.
+  The pattern sign=1, nonzero=0 is never written; unpacking rejects it.
+Row layout: row r holds W = 4 * ceil(K / 64) words; word w holds the codes of
+columns 16*w .. 16*w + 15; codes past column K - 1 are 0 (row padding, so a
+row is a whole number of 16-byte chunks).
+
+Arithmetic: activations arrive as fp16 and are widened to fp64 exactly; codes
+and int8 weights are exact in fp64; the matrix-vector product is a float64
+matmul and the scale multiplies the finished sum. fp16 values are integer
+multiples of 2**-24, so with |x| < 2**9 and K < 2**20 every partial sum is an
+integer multiple of 2**-24 below 2**53 * 2**-24 and the fp64 sum is exact in
+any order; the only rounding is the final multiply by the scale.
+
+Parity pins: see tests/test_oracle.py (exhaustive single-word round trip,
+hand-written format words, the fp16 decode property of the layout, brute force
+over all ternary rows for K <= 8 against exact rational sums, closed forms,
+exact integer matmul for the head, the row-sum and count invariants).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+CODES_PER_WORD = 16
+
+
+def words_per_row(k: int) -> int:
+    """Words per packed row: 4 * ceil(k / 64), i.e. whole 16-byte chunks."""
+    if k <= 0:
+        raise ValueError("k must be positive")
+    return 4 * math.ceil(k / 64)
+
+
+def bit_positions(j: int) -> tuple[int, int]:
+    """(nonzero bit, sign bit) of code j (0..15) inside its word."""
+    if not 0 <= j < CODES_PER_WORD:
+        raise ValueError("code index within a word is 0..15")
+    t, h = divmod(j, 2)
+    return (10 + 16 * h + 2 * t) % 32, (15 + 16 * h + 2 * t) % 32
+
+
+def count_codes(codes: np.ndarray) -> np.ndarray:
+    """[n_minus, n_zero, n_plus, n_invalid] over a whole code tensor (int64)."""
+    c = np.asarray(codes)
+    n_minus = int(np.count_nonzero(c == -1))
+    n_zero = int(np.count_nonzero(c == 0))
+    n_plus = int(np.count_nonzero(c == 1))
+    return np.array([n_minus, n_zero, n_plus, c.size - n_minus - n_zero - n_plus], dtype=np.int64)
+
+
+def pack(codes: np.ndarray):
+    """Pack int8 codes [n, k] (values -1, 0, +1) into the 2-bit layout.
+
+    Returns (packed uint32 [n, W], row_sum int32 [n], counts int64[3] =
+    n_minus, n_zero, n_plus). Raises ValueError on any other code value.
+    Row sums and counts are the per-row metadata and the per-tensor code
+    occupancy (Neutrino-1 8B page: "Where the bytes live", "Inside the coded
+    lane").
+    """
+    codes = np.asarray(codes)
+    if codes.ndim != 2 or codes.dtype != np.int8:
+        raise ValueError("codes must be a 2-D int8 array")
+    n, k = codes.shape
+    stats = count_codes(codes)
+    if stats[3] != 0:
+        raise ValueError(f"{stats[3]} codes outside {{-1, 0, +1}}")
+    w = words_per_row(k)
+    padded = np.zeros((n, w * CODES_PER_WORD), dtype=np.int8)
+    padded[:, :k] = codes
+    grouped = padded.reshape(n, w, CODES_PER_WORD)
+    packed = np.zeros((n, w), dtype=np.uint32)
+    for j in range(CODES_PER_WORD):
+        nz_bit, sign_bit = bit_positions(j)
+        c = grouped[:, :, j]
+        packed |= (c != 0).astype(np.uint32) << np.uint32(nz_bit)
+        packed |= (c < 0).astype(np.uint32) << np.uint32(sign_bit)
+    row_sum = codes.sum(axis=1, dtype=np.int64).astype(np.int32)
+    return packed, row_sum, stats[:3].copy()
+
+
+def unpack(packed: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of pack: uint32 [n, W] -> int8 codes [n, k].
+
+    Raises ValueError on a field with sign=1 and nonzero=0, on a row length
+    that does not match k, or on a nonzero padding code.
+    """
+    packed = np.asarray(packed)
+    if packed.ndim != 2 or packed.dtype != np.uint32:
+        raise ValueError("packed must be a 2-D uint32 array")
+    n, w = packed.shape
+    if w != words_per_row(k):
+        raise ValueError(f"row holds {w} words, k={k} needs {words_per_row(k)}")
+    out = np.zeros((n, w, CODES_PER_WORD), dtype=np.int8)
+    for j in range(CODES_PER_WORD):
+        nz_bit, sign_bit = bit_positions(j)
+        nz = (packed >> np.uint32(nz_bit)) & np.uint32(1)
+        sg = (packed >> np.uint32(sign_bit)) & np.uint32(1)
+        if np.any(sg & ~nz & np.uint32(1)):
+            raise ValueError("field with sign set and nonzero clear")
+        out[:, :, j] = nz.astype(np.int8) * (1 - 2 * sg.astype(np.int8))
+    flat = out.reshape(n, w * CODES_PER_WORD)
+    if np.any(flat[:, k:]):
+        raise ValueError("nonzero padding code")
+    return flat[:, :k].copy()
+
+
+def _as_rows(x: np.ndarray, k: int) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype != np.float16:
+        raise ValueError("activations are fp16")
+    if x.ndim == 1:
+        x = x[None, :]
+    if x.ndim != 2 or x.shape[1] != k:
+        raise ValueError(f"activations must be [m, {k}]")
+    return x.astype(np.float64)
+
+
+def ternary_gemm_small(packed: np.ndarray, scale: np.ndarray, k: int, x: np.ndarray,
+                       row_block: int = 16384) -> np.ndarray:
+    """Y[m, r] = s_r * sum_j c_rj * X[m, j] in fp64, for M activation rows.
+
+    Unpacks the codes (in row blocks to bound memory), widens them and X to
+    fp64, multiplies, then applies the per-row scale.
+    """
+    xs = _as_rows(x, k)
+    scale = np.asarray(scale)
+    if scale.dtype != np.float32 or scale.shape != (packed.shape[0],):
+        raise ValueError("scale must be fp32 [n]")
+    n = packed.shape[0]
+    y = np.empty((xs.shape[0], n), dtype=np.float64)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        c = unpack(packed[r0:r1], k).astype(np.float64)
+        sums = xs @ c.T
+        y[:, r0:r1] = sums * scale[r0:r1].astype(np.float64)[None, :]
+    return y
+
+
+def ternary_gemv(packed: np.ndarray, scale: np.ndarray, k: int, x: np.ndarray) -> np.ndarray:
+    """y_r = s_r * sum_j c_rj * x_j in fp64 (one activation row, M = 1)."""
+    x = np.asarray(x)
+    if x.ndim != 1:
+        raise ValueError("ternary_gemv takes one activation row")
+    return ternary_gemm_small(packed, scale, k, x[None, :])[0]
+
+
+def int8_head_gemv(w: np.ndarray, scale: np.ndarray, x: np.ndarray, row_block: int = 8192) -> np.ndarray:
+    """Y[m, v] = s_v * sum_j w_vj * X[m, j] in fp64 (int8 head, one scale per row)."""
+    w = np.asarray(w)
+    if w.ndim != 2 or w.dtype != np.int8:
+        raise ValueError("head weights must be a 2-D int8 array")
+    n, k = w.shape
+    xs = _as_rows(x, k)
+    scale = np.asarray(scale)
+    if scale.dtype != np.float32 or scale.shape != (n,):
+        raise ValueError("scale must be fp32 [n]")
+    y = np.empty((xs.shape[0], n), dtype=np.float64)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        sums = xs @ w[r0:r1].astype(np.float64).T
+        y[:, r0:r1] = sums * scale[r0:r1].astype(np.float64)[None, :]
+    return y

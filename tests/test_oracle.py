@@ -1,0 +1,251 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: a hand-derived word of the
+layout (tests/golden/format_words.txt), a property of IEEE fp16 that the
+layout is built around, exact rational arithmetic (fractions.Fraction),
+Python's exactly rounded math.fsum, exact integer matmul, closed forms, or a
+count printed on the Neutrino-1 8B model page.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import read_format_words, read_key_values
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# --------------------------------------------------------------------------
+# Layout
+# --------------------------------------------------------------------------
+def test_words_per_row():
+    assert oracle.words_per_row(1) == 4
+    assert oracle.words_per_row(64) == 4
+    assert oracle.words_per_row(65) == 8
+    assert oracle.words_per_row(4096) == 256
+    assert oracle.words_per_row(12288) == 768
+    with pytest.raises(ValueError):
+        oracle.words_per_row(0)
+
+
+def test_bit_positions_cover_word_once():
+    seen = [p for j in range(16) for p in oracle.bit_positions(j)]
+    assert sorted(seen) == list(range(32))
+
+
+@pytest.mark.parametrize("case", range(len(read_format_words())))
+def test_golden_words(case):
+    k, codes, words = read_format_words()[case]
+    packed, row_sum, counts = oracle.pack(codes[None, :])
+    assert packed.shape == (1, words.size)
+    assert [f"{v:08X}" for v in packed[0]] == [f"{v:08X}" for v in words]
+    assert np.array_equal(oracle.unpack(words[None, :], k)[0], codes)
+    assert row_sum[0] == int(codes.astype(np.int64).sum())
+
+
+def test_fp16_decode_property():
+    """rotr(word, 2t) & 0x84008400, read as two fp16 values, equals
+    (c[2t], c[2t+1]) * 2**-14: bit 10/26 set gives the smallest normal fp16
+    exponent, bit 15/31 is the fp16 sign."""
+    codes = synth.ternary_codes(11, 64, 256)
+    packed, _, _ = oracle.pack(codes)
+    words = packed.reshape(-1).astype(np.uint64)
+    c = codes.reshape(-1, 16).astype(np.float64)
+    for t in range(8):
+        r = 2 * t
+        rot = ((words >> np.uint64(r)) | (words << np.uint64(32 - r))) & np.uint64(0xFFFFFFFF) if r else words
+        m = (rot & np.uint64(0x84008400)).astype(np.uint32)
+        halves = m.view(np.float16).reshape(-1, 2).astype(np.float64) * 2.0**14
+        assert np.array_equal(halves[:, 0], c[:, 2 * t])
+        assert np.array_equal(halves[:, 1], c[:, 2 * t + 1])
+
+
+@pytest.mark.slow
+def test_exhaustive_single_word_round_trip():
+    """All 3**16 code vectors of one word survive pack -> unpack, hence pack
+    is injective on words; each pack output has only canonical fields."""
+    n_all = 3 ** 16
+    block = 3 ** 14
+    digits = (np.arange(block, dtype=np.int64)[:, None] // (3 ** np.arange(14, dtype=np.int64))[None, :]) % 3
+    low = (digits - 1).astype(np.int8)
+    seen = 0
+    for hi in itertools.product((-1, 0, 1), repeat=2):
+        codes = np.empty((block, 16), dtype=np.int8)
+        codes[:, :14] = low
+        codes[:, 14] = hi[0]
+        codes[:, 15] = hi[1]
+        packed, _, _ = oracle.pack(codes)
+        assert not np.any(packed[:, 1:])
+        back = oracle.unpack(packed, 16)
+        assert np.array_equal(back, codes)
+        seen += block
+    assert seen == n_all
+
+
+def test_unpack_rejects_noncanonical_and_padding():
+    k = 16
+    for j in range(16):
+        nz, sg = oracle.bit_positions(j)
+        bad = np.zeros((1, 4), dtype=np.uint32)
+        bad[0, 0] = np.uint32(1 << sg)
+        with pytest.raises(ValueError):
+            oracle.unpack(bad, k)
+    pad = np.zeros((1, 4), dtype=np.uint32)
+    pad[0, 1] = np.uint32(1 << 10)
+    with pytest.raises(ValueError):
+        oracle.unpack(pad, 16)
+
+
+def test_pack_rejects_invalid_codes():
+    codes = np.zeros((2, 8), dtype=np.int8)
+    codes[1, 3] = 2
+    with pytest.raises(ValueError):
+        oracle.pack(codes)
+    assert oracle.count_codes(codes).tolist() == [0, 15, 0, 1]
+
+
+def test_row_sum_and_counts_from_bits():
+    """row_sum = popcount(nonzero bits) - 2 * popcount(sign bits) per row, and
+    the three counts add up to N*K and match a histogram of the codes."""
+    codes = synth.ternary_codes(5, 37, 333)
+    packed, row_sum, counts = oracle.pack(codes)
+    nz_mask = sum(1 << oracle.bit_positions(j)[0] for j in range(16))
+    sg_mask = sum(1 << oracle.bit_positions(j)[1] for j in range(16))
+    pop = np.vectorize(lambda v: bin(int(v)).count("1"))
+    nz = pop(packed & np.uint32(nz_mask)).sum(axis=1)
+    sg = pop(packed & np.uint32(sg_mask)).sum(axis=1)
+    assert np.array_equal(row_sum.astype(np.int64), nz - 2 * sg)
+    hist = np.bincount(codes.reshape(-1).astype(np.int64) + 1, minlength=3)
+    assert counts.tolist() == hist.tolist()
+    assert int(counts.sum()) == codes.size
+
+
+# --------------------------------------------------------------------------
+# Ternary GEMV arithmetic
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 7, 8])
+def test_brute_force_all_rows_exact(k):
+    """Every ternary row of length k (3**k rows) against exact rational sums,
+    rounded once by the scale multiply."""
+    rows = np.array(list(itertools.product((-1, 0, 1), repeat=k)), dtype=np.int8)
+    x = synth.activations(100 + k, 1, k)[0] * np.float16(3.0)
+    s = synth.row_scales(200 + k, rows.shape[0])
+    packed, _, _ = oracle.pack(rows)
+    y = oracle.ternary_gemv(packed, s, k, x)
+    xf = [Fraction(float(v)) for v in x]
+    for r in range(rows.shape[0]):
+        exact = sum((int(c) * xv for c, xv in zip(rows[r], xf)), Fraction(0))
+        assert y[r] == float(Fraction(float(s[r])) * exact)
+
+
+def test_fsum_exact_large_k():
+    """Rows with K = 12288 against math.fsum (exactly rounded) of c_j * x_j."""
+    k = 12288
+    codes = synth.ternary_codes(7, 12, k)
+    x = synth.activations(8, 1, k)[0]
+    s = synth.row_scales(9, 12)
+    packed, _, _ = oracle.pack(codes)
+    y = oracle.ternary_gemv(packed, s, k, x)
+    xd = x.astype(np.float64)
+    for r in range(12):
+        ref = math.fsum(float(c) * float(v) for c, v in zip(codes[r], xd))
+        assert y[r] == float(s[r]) * ref
+
+
+def test_closed_forms():
+    k, n = 200, 200
+    x = synth.activations(21, 1, k)[0]
+    s = synth.row_scales(22, n)
+    xd = x.astype(np.float64)
+    zero = np.zeros((n, k), dtype=np.int8)
+    assert np.all(oracle.ternary_gemv(oracle.pack(zero)[0], s, k, x) == 0.0)
+    ones = np.ones((n, k), dtype=np.int8)
+    assert np.allclose(oracle.ternary_gemv(oracle.pack(ones)[0], s, k, x),
+                       s.astype(np.float64) * math.fsum(xd), rtol=1e-15, atol=0)
+    eye = np.eye(n, k, dtype=np.int8)
+    assert np.array_equal(oracle.ternary_gemv(oracle.pack(eye)[0], s, k, x), s.astype(np.float64) * xd)
+    codes = synth.ternary_codes(23, n, k)
+    y = oracle.ternary_gemv(oracle.pack(codes)[0], s, k, x)
+    assert np.array_equal(oracle.ternary_gemv(oracle.pack(-codes)[0], s, k, x), -y)
+    perm = np.random.Generator(np.random.PCG64(24)).permutation(k)
+    assert np.array_equal(oracle.ternary_gemv(oracle.pack(codes[:, perm])[0], s, k, x[perm]), y)
+
+
+def test_small_m_rows_equal_single_rows():
+    k, n = 300, 50
+    codes = synth.ternary_codes(31, n, k)
+    s = synth.row_scales(32, n)
+    xs = synth.activations(33, 8, k)
+    packed = oracle.pack(codes)[0]
+    ym = oracle.ternary_gemm_small(packed, s, k, xs)
+    for m in range(8):
+        assert np.array_equal(ym[m], oracle.ternary_gemv(packed, s, k, xs[m]))
+
+
+def test_integer_probe_exact():
+    """Integer activations and power-of-two scales: y is an exact integer
+    multiple of the scale, equal to the integer matmul."""
+    k, n = 4096, 64
+    codes = synth.ternary_codes(41, n, k)
+    x = synth.probe_activations(42, 1, k)[0]
+    s = synth.pow2_scales(43, n)
+    y = oracle.ternary_gemv(oracle.pack(codes)[0], s, k, x)
+    ref = codes.astype(np.int64) @ x.astype(np.int64)
+    assert np.array_equal(y, ref.astype(np.float64) * s.astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# int8 head
+# --------------------------------------------------------------------------
+def test_head_integer_exact():
+    n, k = 96, 4096
+    w = synth.int8_full_range(51, n, k)
+    x = synth.probe_activations(52, 3, k)
+    s = synth.pow2_scales(53, n)
+    y = oracle.int8_head_gemv(w, s, x)
+    ref = x.astype(np.int64) @ w.astype(np.int64).T
+    assert np.array_equal(y, ref.astype(np.float64) * s.astype(np.float64)[None, :])
+
+
+def test_head_fsum():
+    n, k = 10, 4096
+    w = synth.head_weights(61, n, k)
+    x = synth.activations(62, 1, k)[0]
+    s = synth.row_scales(63, n)
+    y = oracle.int8_head_gemv(w, s, x)[0]
+    for r in range(n):
+        ref = math.fsum(float(a) * float(b) for a, b in zip(w[r], x.astype(np.float64)))
+        assert y[r] == float(s[r]) * ref
+
+
+def test_head_chunking_invariant():
+    n, k = 1000, 64
+    w = synth.head_weights(71, n, k)
+    x = synth.activations(72, 2, k)
+    s = synth.row_scales(73, n)
+    assert np.array_equal(oracle.int8_head_gemv(w, s, x, row_block=7), oracle.int8_head_gemv(w, s, x))
+
+
+# --------------------------------------------------------------------------
+# Geometry printed on the model page
+# --------------------------------------------------------------------------
+def test_geometry_matches_printed_parameter_count():
+    g = read_key_values("neutrino_geometry.txt")
+    coded = sum(n * k for n, k in synth.SHAPES.values()) * g["layers"]
+    emb = 2 * g["vocab"] * g["hidden"]
+    norms = g["layers"] * (2 * g["hidden"] + 2 * g["head_dim"]) + g["hidden"]
+    assert g["layers"] * 4 + 1 == g["norm_tensors"]
+    assert coded + emb + norms == g["parameters"]
+    assert round(coded / 1e9, 2) == 6.95
+    # The shipped lane is exactly 3 bits per coded weight; this layout is 2.
+    assert g["shipped_coded_bytes_per_layer"] * 8 == 3 * (coded // g["layers"])
+    packed_layer = sum(synth.words_bytes(n, k) for n, k in synth.SHAPES.values())
+    assert packed_layer == 48234496
+    assert synth.HEAD_SHAPE == (g["vocab"], g["hidden"])
