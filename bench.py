@@ -1,0 +1,310 @@
+"""Benchmark of the packed ternary GEMV path on one MI355X.
+
+Headline (one JSON line on stdout): achieved HBM GB/s of the feed-forward
+ternary GEMVs at M = 1 (gate and up 12288 x 4096, down 4096 x 12288; codes
+with 71 % zeros for gate/down in layers 1-3 and 62.63 % elsewhere, Neutrino-1 8B
+model page, "Inside the coded lane"). One step = one decoder layer's three FFN
+GEMVs on fresh activations; steps walk a pool of 36 distinct synthetic layers
+(1.37 GB of packed weights, far above the 256 MB Infinity Cache), so every
+step streams its weights from HBM.
+
+Also reported under "extra": microseconds per linear, per decoder layer (7
+linears) and per full decode step (36 layers + int8 head 151,936 x 4,096), the
+head alone, and the small-M (speculative verify) shapes, plus the streaming
+read ceiling of a plain copy (torch) at the same byte count.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "achieved HBM GB/s (% of peak) for packed-ternary GEMV, M=1; µs per decoder layer"
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_ternary_gemv_ffn_m1.json")
+KERNEL_SOURCES = ("packed_bit_gemv_amd/csrc/ternary.hip", "packed_bit_gemv_amd/csrc/pbg_device.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ternary_bytes(n: int, k: int, m: int = 1) -> int:
+    """Algorithmic bytes of one call: packed words + fp32 scales + fp16 x + fp32 y."""
+    return synth.words_bytes(n, k) + 4 * n + 2 * m * k + 4 * m * n
+
+
+def head_bytes(n: int, k: int, m: int = 1) -> int:
+    return n * k + 4 * n + 2 * m * k + 4 * m * n
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Model:
+    """36 synthetic decoder layers of packed ternary linears plus the int8 head."""
+
+    def __init__(self, pbg, torch, device, layers: int, with_head: bool, projs=synth.PROJECTIONS):
+        self.layers = []
+        stats_buf = torch.empty(4, dtype=torch.int64, device=device)
+        for l in range(layers):
+            lay = {}
+            for p in projs:
+                n, k = synth.SHAPES[p]
+                seed = synth.tensor_seed(l, p)
+                codes = synth.ternary_codes_device(seed, n, k, synth.code_dist(l, p), device)
+                packed, _, _ = pbg.pack_ternary(codes, stats=stats_buf, check=False)
+                del codes
+                lay[p] = (packed, synth.row_scales_device(seed, n, device), n, k)
+            self.layers.append(lay)
+        self.head = None
+        if with_head:
+            n, k = synth.HEAD_SHAPE
+            self.head = (synth.head_weights_device(synth.SEED_HEAD, n, k, device),
+                         synth.row_scales_device(synth.SEED_HEAD, n, device), n, k)
+        torch.cuda.synchronize()
+
+
+def time_region(torch, fn, steps: int, warmup: int):
+    """Runs fn(i) warmup times, then times exactly `steps` calls; ms per step."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(budget_s: float):
+    """The CPU oracle timed on this host on a bounded sample of the workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:
+        threads = 1
+    rows = 1024
+    samples = []
+    for p in ("gate", "up", "down"):
+        n, k = synth.SHAPES[p]
+        codes = synth.ternary_codes(synth.tensor_seed(1, p), rows, k, synth.code_dist(1, p))
+        samples.append((oracle.pack(codes)[0], synth.row_scales(synth.tensor_seed(1, p), rows), k,
+                        synth.activations(synth.x_seed(0), 1, k)[0], rows))
+    done_bytes = 0
+    reps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for packed, s, k, x, r in samples:
+            oracle.ternary_gemv(packed, s, k, x)
+            done_bytes += ternary_bytes(r, k)
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{reps} passes over the first {rows} rows of layer-1 gate, up and down (M=1), "
+                   f"{dt:.1f} s; unpack in NumPy (1 thread) + fp64 matvec in BLAS ({threads} threads)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the packed ternary GEMV path has no multi-GPU part here "
+              "(every published figure is single-device). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import packed_bit_gemv_amd as pbg
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    log(f"device: {torch.cuda.get_device_name(device)}")
+    t0 = time.time()
+    model = Model(pbg, torch, device, args.layers, with_head=not args.no_extra,
+                  projs=synth.PROJECTIONS if not args.no_extra else ("gate", "up", "down"))
+    log(f"model built in {time.time() - t0:.1f} s")
+
+    ffn = ("gate", "up", "down")
+    xs = {k: torch.from_numpy(synth.activations(synth.x_seed(0), 8, k)).to(device) for k in (synth.HIDDEN, synth.FFN)}
+    ys = {p: torch.empty((8, synth.SHAPES[p][0]), dtype=torch.float32, device=device) for p in synth.PROJECTIONS}
+    L = len(model.layers)
+
+    def linear(layer, p, m=1):
+        packed, s, n, k = model.layers[layer][p]
+        if m == 1:
+            pbg.ternary_gemv(packed, s, k, xs[k][0], ys[p][0])
+        else:
+            pbg.ternary_gemm_small(packed, s, k, xs[k][:m], ys[p][:m])
+
+    def ffn_step(i):
+        for p in ffn:
+            linear(i % L, p)
+
+    # ---- headline: FFN GEMVs at M = 1, timed region ------------------------
+    bytes_step = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)
+    for i in range(args.warmup):
+        ffn_step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * 3 * args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    j = 0
+    for i in range(args.steps):
+        layer = (args.warmup + i) % L
+        for p in ffn:
+            ev[j].record(stream)
+            linear(layer, p)
+            ev[j + 1].record(stream)
+            j += 2
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    launch_ms = np.array([ev[2 * q].elapsed_time(ev[2 * q + 1]) for q in range(3 * args.steps)])
+    per_proj_us = {p: float(np.mean(launch_ms[i::3]) * 1e3) for i, p in enumerate(ffn)}
+    avg_launch_us = float(launch_ms.mean() * 1e3)
+    achieved = bytes_step / 3 / (avg_launch_us * 1e-6) / 1e9
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    log(f"ffn step {ms_step * 1e3:.2f} us, {value:.1f} GB/s; per launch {per_proj_us}")
+
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    extra = {"us_per_launch_event": {p: round(v, 3) for p, v in per_proj_us.items()},
+             "layers_in_pool": L, "pool_bytes_packed": bytes_step * L}
+
+    if not args.no_extra:
+        K, W = max(20, args.steps // 4), 5
+        # per-linear (M = 1), walking the layer pool
+        for p in synth.PROJECTIONS:
+            ms = time_region(torch, lambda i, p=p: linear(i % L, p), K, W)
+            n, k = synth.SHAPES[p]
+            extra[f"{p}_m1_us"] = round(ms * 1e3, 3)
+            extra[f"{p}_m1_GBs"] = round(ternary_bytes(n, k) / (ms * 1e-3) / 1e9, 1)
+
+        def layer_step(i, m=1):
+            for p in synth.PROJECTIONS:
+                linear(i % L, p, m)
+
+        ms = time_region(torch, layer_step, K, W)
+        layer_bytes = sum(ternary_bytes(*synth.SHAPES[p]) for p in synth.PROJECTIONS)
+        extra["layer_m1_us"] = round(ms * 1e3, 3)
+        extra["layer_m1_GBs"] = round(layer_bytes / (ms * 1e-3) / 1e9, 1)
+
+        hw, hs, hn, hk = model.head
+        yh = torch.empty((8, hn), dtype=torch.float32, device=device)
+
+        def head(m=1):
+            pbg.int8_head_gemv(hw, hs, xs[hk][:m], yh[:m])
+
+        for m in (1, 2, 4, 7, 8):
+            ms = time_region(torch, lambda i, m=m: head(m), 10, 2)
+            extra[f"head_m{m}_us"] = round(ms * 1e3, 2)
+            extra[f"head_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
+
+        def decode_step(i):
+            for l in range(L):
+                for p in synth.PROJECTIONS:
+                    linear(l, p)
+            head(1)
+
+        ms = time_region(torch, decode_step, 5, 1)
+        dec_bytes = layer_bytes * L + head_bytes(hn, hk)
+        extra["decode_step_m1_us"] = round(ms * 1e3, 1)
+        extra["decode_step_m1_GBs"] = round(dec_bytes / (ms * 1e-3) / 1e9, 1)
+
+        for m in (2, 4, 7, 8):
+            ms = time_region(torch, lambda i, m=m: layer_step(i, m), K, W)
+            lb = sum(ternary_bytes(*synth.SHAPES[p], m) for p in synth.PROJECTIONS)
+            extra[f"layer_m{m}_us"] = round(ms * 1e3, 3)
+            extra[f"layer_m{m}_GBs"] = round(lb / (ms * 1e-3) / 1e9, 1)
+
+        # streaming-read ceiling at the FFN byte count: torch copy of a pool
+        nbytes = synth.words_bytes(*synth.SHAPES["gate"])
+        pool = [torch.empty(nbytes // 4, dtype=torch.int32, device=device) for _ in range(48)]
+        dst = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+        ms = time_region(torch, lambda i: dst.copy_(pool[i % 48]), 60, 10)
+        extra["copy_12.6MB_us"] = round(ms * 1e3, 3)
+        extra["copy_12.6MB_GBs_read_plus_write"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+        del pool, dst
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16*ternary->f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "ffn_gate_up_down_m1",
+            "shapes": {p: list(synth.SHAPES[p]) for p in ffn},
+            "m": 1,
+            "layers_in_pool": L,
+            "us_per_step": round(ms_step * 1e3, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "ternary_gemv_kernel",
+            "avg_launch_us": round(avg_launch_us, 3),
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
+        "extra": extra,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

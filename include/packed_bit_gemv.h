@@ -1,0 +1,140 @@
+/*
+ * packed_bit_gemv.h - C ABI of libpackedbitgemv.so, the MI355X (gfx950)
+ * decode-time matrix-vector kernels for bit-packed ternary weights and for an
+ * int8 output head.
+ *
+ * What is computed (Neutrino-1 8B model page, English text on bittide):
+ *   - every transformer linear is stored as ternary codes c in {-1, 0, +1}
+ *     with a scale and a row sum per row, and is decoded inside the matrix
+ *     kernels, never stored as fp16/fp32 weights (introduction; "Where the
+ *     bytes live"; "Inside the coded lane");
+ *   - the untied output head is an int8 tensor with one scale per row
+ *     ("Where the bytes live");
+ *   - a speculative verify pass scores a drafted run of tokens in one forward
+ *     pass ("speculative" section), i.e. the same products for M <= 8 rows.
+ *
+ * Packed layout (this library's own; the page calls its format proprietary):
+ *   - 2 bits per code, 16 codes per little-endian uint32 word;
+ *   - code j (0..15) of a word: pair t = j / 2, half h = j % 2;
+ *       nonzero bit at (10 + 16*h + 2*t) mod 32,
+ *       sign bit    at (15 + 16*h + 2*t) mod 32;
+ *     +1 = (nonzero 1, sign 0), -1 = (1, 1), 0 = (0, 0); (0, 1) never occurs.
+ *     Rotating a word right by 2t and masking with 0x84008400 leaves two
+ *     IEEE fp16 values equal to c[2t] * 2^-14 and c[2t+1] * 2^-14.
+ *   - row r of an N x K matrix is pbg_words_per_row(K) = 4 * ceil(K / 64)
+ *     consecutive words (a whole number of 16-byte chunks); word w holds the
+ *     codes of columns 16w .. 16w+15; codes past column K-1 are 0.
+ *   - per row: an fp32 scale s_r and an int32 row sum sum_j c_rj.
+ *
+ * Conventions for every entry point:
+ *   - all array pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them, and holds no global state;
+ *   - work is enqueued on the caller's `stream` (0 = the null stream) and
+ *     the call returns without waiting, except where stated;
+ *   - arguments are validated before any HIP call; on a validation error
+ *     nothing is enqueued and a negative PBG_ERR_* code is returned;
+ *   - outputs must not overlap inputs;
+ *   - activations x are IEEE fp16 bit patterns (uint16_t), row-major [m][k];
+ *     they must be finite: a zero code contributes 0 * x_j;
+ *   - outputs y are fp32, row-major [m][n]; accumulation is fp32 in an
+ *     unspecified order (any order meets |y - y_exact| <= 1e-3 * s_r *
+ *     sum_j |x_j| for K below about 16,000).
+ */
+#ifndef PACKED_BIT_GEMV_H
+#define PACKED_BIT_GEMV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PBG_ABI_VERSION 1
+
+/* Return codes. */
+#define PBG_OK 0
+#define PBG_ERR_NULL (-1)    /* a required pointer is NULL */
+#define PBG_ERR_SHAPE (-2)   /* n, k or m out of range */
+#define PBG_ERR_ALIGN (-3)   /* a pointer lacks its required alignment */
+#define PBG_ERR_CODE (-4)    /* pack input held a value outside {-1, 0, +1} */
+#define PBG_ERR_HIP (-5)     /* a HIP launch or copy failed */
+
+/* Limits: 1 <= n <= PBG_MAX_N, 1 <= k <= PBG_MAX_K, 1 <= m <= PBG_MAX_M. */
+#define PBG_MAX_N 16777216LL
+#define PBG_MAX_K 16777216LL
+#define PBG_MAX_M 8
+
+/* Version of this ABI (PBG_ABI_VERSION of the built library). */
+int pbg_abi_version(void);
+
+/* Static message for a return code; never NULL. */
+const char* pbg_strerror(int code);
+
+/* Words per packed row for k columns: 4 * ceil(k / 64); 0 if k <= 0. */
+int64_t pbg_words_per_row(int64_t k);
+
+/*
+ * pack_ternary - load-time encoding of one coded linear.
+ * Source: Neutrino-1 8B model page, "Where the bytes live" (ternary codes with
+ * per-row scales and row sums) and "Inside the coded lane" (code occupancy).
+ *
+ *   codes    [n][k] int8, row-major, values -1, 0, +1 (any alignment)
+ *   packed   [n][pbg_words_per_row(k)] uint32 out, 16-byte aligned
+ *   row_sum  [n] int32 out: sum_j codes[r][j] over valid codes
+ *   stats    [4] int64 out, device, 8-byte aligned: n_minus, n_zero, n_plus,
+ *            n_invalid over the whole tensor (zeroed by this call)
+ *   stats_host  NULL, or a host array of 4 int64: then the call waits for the
+ *            stream, copies stats there and returns PBG_ERR_CODE if
+ *            n_invalid > 0
+ * An invalid code is counted and packed as 0 and adds nothing to row_sum.
+ */
+int pack_ternary(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, int32_t* row_sum,
+                 int64_t* stats, int64_t* stats_host, hipStream_t stream);
+
+/*
+ * ternary_gemv - y[r] = scale[r] * sum_j c[r][j] * x[j], one activation row.
+ * Source: Neutrino-1 8B model page, introduction (codes decoded inside the
+ * matrix kernels; decode bound by bytes moved per token) and "Where the bytes
+ * live" (per-row scale).
+ *
+ *   packed  [n][pbg_words_per_row(k)] uint32, 16-byte aligned
+ *   scale   [n] fp32, 4-byte aligned
+ *   x       [k] fp16 bits, 2-byte aligned
+ *   y       [n] fp32 out, 4-byte aligned
+ */
+int ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                 float* y, hipStream_t stream);
+
+/*
+ * ternary_gemm_small - Y[i][r] = scale[r] * sum_j c[r][j] * X[i][j] for
+ * 1 <= m <= 8 activation rows, reading each weight word once.
+ * Source: Neutrino-1 8B model page, "speculative" section (the 8B scores a
+ * drafted run of up to six tokens plus one in a single forward pass).
+ *
+ *   packed, scale  as ternary_gemv
+ *   x       [m][k] fp16 bits, 2-byte aligned
+ *   y       [m][n] fp32 out, 4-byte aligned
+ */
+int ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                       int64_t m, float* y, hipStream_t stream);
+
+/*
+ * int8_head_gemv - Y[i][v] = scale[v] * sum_j w[v][j] * X[i][j] for the int8
+ * output head, 1 <= m <= 8 activation rows.
+ * Source: Neutrino-1 8B model page, "Where the bytes live" (untied int8
+ * output head of 151,936 x 4,096 with one scale per row).
+ *
+ *   w       [n][k] int8, row-major, 16-byte aligned
+ *   scale   [n] fp32, 4-byte aligned
+ *   x       [m][k] fp16 bits, 2-byte aligned
+ *   y       [m][n] fp32 out, 4-byte aligned
+ */
+int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+                   float* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACKED_BIT_GEMV_H */

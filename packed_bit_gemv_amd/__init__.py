@@ -1,0 +1,25 @@
+"""MI355X (gfx950) packed ternary GEMV: HIP kernels behind a C ABI.
+
+The compute path is libpackedbitgemv.so (built from csrc/ by build.py); this
+package only binds it. Packed words are carried in torch.int32 tensors (same
+bits as the uint32 words of the C ABI).
+"""
+from .binding import (  # noqa: F401
+    PbgError,
+    int8_head_gemv,
+    lib,
+    pack_ternary,
+    ternary_gemm_small,
+    ternary_gemv,
+    words_per_row,
+)
+
+__all__ = [
+    "PbgError",
+    "int8_head_gemv",
+    "lib",
+    "pack_ternary",
+    "ternary_gemm_small",
+    "ternary_gemv",
+    "words_per_row",
+]

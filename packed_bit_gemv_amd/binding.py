@@ -1,0 +1,188 @@
+"""ctypes binding of libpackedbitgemv.so.
+
+Argument marshalling only: every function checks tensor placement, dtype and
+shape, passes raw device pointers and the current HIP stream to the C entry
+point of the same name, and raises PbgError on a nonzero return code. All
+computation happens in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+from .build import LIB_PATH
+
+PBG_ERR_CODE = -4
+
+_c_int = ctypes.c_int
+_c_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+# (restype, argtypes) of every entry point declared in include/packed_bit_gemv.h.
+_SIGNATURES = {
+    "pbg_abi_version": (_c_int, []),
+    "pbg_strerror": (ctypes.c_char_p, [_c_int]),
+    "pbg_words_per_row": (_c_i64, [_c_i64]),
+    "pack_ternary": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "ternary_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "ternary_gemm_small": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "int8_head_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
+}
+
+
+class PbgError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m packed_bit_gemv_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/packed_bit_gemv.h."""
+    path = os.path.join(os.path.dirname(os.path.dirname(LIB_PATH)), "include", "packed_bit_gemv.h")
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise PbgError(fn, rc, lib().pbg_strerror(rc).decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def words_per_row(k: int) -> int:
+    return int(lib().pbg_words_per_row(int(k)))
+
+
+def pack_ternary(codes: torch.Tensor, packed: torch.Tensor | None = None, row_sum: torch.Tensor | None = None,
+                 stats: torch.Tensor | None = None, check: bool = True):
+    """Pack int8 codes [n, k] on the GPU. Returns (packed, row_sum, stats).
+
+    stats holds n_minus, n_zero, n_plus, n_invalid. With check=True the call
+    waits for the stream and raises PbgError if any code is outside {-1,0,1}.
+    """
+    _dev(codes, "codes", torch.int8)
+    if codes.dim() != 2:
+        raise ValueError("codes must be [n, k]")
+    n, k = codes.shape
+    dev = codes.device
+    if packed is None:
+        packed = torch.empty((n, words_per_row(k)), dtype=torch.int32, device=dev)
+    if row_sum is None:
+        row_sum = torch.empty((n,), dtype=torch.int32, device=dev)
+    if stats is None:
+        stats = torch.empty((4,), dtype=torch.int64, device=dev)
+    _dev(packed, "packed", torch.int32)
+    _dev(row_sum, "row_sum", torch.int32)
+    _dev(stats, "stats", torch.int64)
+    if tuple(packed.shape) != (n, words_per_row(k)) or tuple(row_sum.shape) != (n,) or stats.numel() != 4:
+        raise ValueError("output shapes do not match codes")
+    host = (ctypes.c_int64 * 4)() if check else None
+    rc = lib().pack_ternary(codes.data_ptr(), n, k, packed.data_ptr(), row_sum.data_ptr(), stats.data_ptr(),
+                            ctypes.addressof(host) if host is not None else None, _stream(codes))
+    _check("pack_ternary", rc)
+    return packed, row_sum, stats
+
+
+def _ternary_args(packed, scale, k, x):
+    _dev(packed, "packed", torch.int32)
+    _dev(scale, "scale", torch.float32)
+    _dev(x, "x", torch.float16)
+    n = packed.shape[0]
+    if packed.dim() != 2 or packed.shape[1] != words_per_row(k):
+        raise ValueError(f"packed must be [n, {words_per_row(k)}] for k={k}")
+    if tuple(scale.shape) != (n,):
+        raise ValueError("scale must be [n]")
+    return n
+
+
+def ternary_gemv(packed: torch.Tensor, scale: torch.Tensor, k: int, x: torch.Tensor,
+                 y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[r] = scale[r] * sum_j c[r, j] * x[j]; x is fp16 [k], y fp32 [n]."""
+    n = _ternary_args(packed, scale, k, x)
+    if tuple(x.shape) != (k,):
+        raise ValueError(f"x must be [{k}]")
+    if y is None:
+        y = torch.empty((n,), dtype=torch.float32, device=packed.device)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != (n,):
+        raise ValueError("y must be [n]")
+    rc = lib().ternary_gemv(packed.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), y.data_ptr(), _stream(packed))
+    _check("ternary_gemv", rc)
+    return y
+
+
+def ternary_gemm_small(packed: torch.Tensor, scale: torch.Tensor, k: int, x: torch.Tensor,
+                       y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[i, r] = scale[r] * sum_j c[r, j] * X[i, j]; X fp16 [m, k], m <= 8; Y fp32 [m, n]."""
+    n = _ternary_args(packed, scale, k, x)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=packed.device)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != (m, n):
+        raise ValueError("y must be [m, n]")
+    rc = lib().ternary_gemm_small(packed.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, y.data_ptr(),
+                                  _stream(packed))
+    _check("ternary_gemm_small", rc)
+    return y
+
+
+def int8_head_gemv(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor,
+                   y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[i, v] = scale[v] * sum_j w[v, j] * X[i, j]; w int8 [n, k], X fp16 [m, k]; Y fp32 [m, n]."""
+    _dev(w, "w", torch.int8)
+    _dev(scale, "scale", torch.float32)
+    _dev(x, "x", torch.float16)
+    if w.dim() != 2:
+        raise ValueError("w must be [n, k]")
+    n, k = w.shape
+    if tuple(scale.shape) != (n,):
+        raise ValueError("scale must be [n]")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != (m, n):
+        raise ValueError("y must be [m, n]")
+    rc = lib().int8_head_gemv(w.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, y.data_ptr(), _stream(w))
+    _check("int8_head_gemv", rc)
+    return y

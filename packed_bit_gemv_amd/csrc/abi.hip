@@ -1,0 +1,80 @@
+// C ABI of libpackedbitgemv: argument validation (before any HIP call),
+// error mapping and dispatch to the gfx950 launchers.
+#include "packed_bit_gemv.h"
+#include "pbg_internal.hpp"
+
+namespace {
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+bool bad_nk(int64_t n, int64_t k) { return n < 1 || n > PBG_MAX_N || k < 1 || k > PBG_MAX_K; }
+
+bool bad_m(int64_t m) { return m < 1 || m > PBG_MAX_M; }
+
+int finish(hipError_t launch_status) {
+  if (launch_status != hipSuccess) return PBG_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? PBG_OK : PBG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pbg_abi_version(void) { return PBG_ABI_VERSION; }
+
+const char* pbg_strerror(int code) {
+  switch (code) {
+    case PBG_OK: return "ok";
+    case PBG_ERR_NULL: return "a required pointer is NULL";
+    case PBG_ERR_SHAPE: return "n, k or m out of range";
+    case PBG_ERR_ALIGN: return "a pointer lacks its required alignment";
+    case PBG_ERR_CODE: return "pack input held a value outside {-1, 0, +1}";
+    case PBG_ERR_HIP: return "a HIP launch or copy failed";
+    default: return "unknown error code";
+  }
+}
+
+int64_t pbg_words_per_row(int64_t k) { return pbg::words_per_row(k); }
+
+int pack_ternary(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, int32_t* row_sum, int64_t* stats,
+                 int64_t* stats_host, hipStream_t stream) {
+  if (!codes || !packed || !row_sum || !stats) return PBG_ERR_NULL;
+  if (bad_nk(n, k)) return PBG_ERR_SHAPE;
+  if (misaligned(packed, 16) || misaligned(row_sum, 4) || misaligned(stats, 8)) return PBG_ERR_ALIGN;
+  (void)hipGetLastError();  // clear a stale error so the status below is this call's
+  int rc = finish(pbg::launch_pack(codes, n, k, packed, row_sum, stats, stream));
+  if (rc != PBG_OK || !stats_host) return rc;
+  if (hipMemcpyAsync(stats_host, stats, 4 * sizeof(int64_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PBG_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PBG_ERR_HIP;
+  return stats_host[3] > 0 ? PBG_ERR_CODE : PBG_OK;
+}
+
+int ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                 hipStream_t stream) {
+  if (!packed || !scale || !x || !y) return PBG_ERR_NULL;
+  if (bad_nk(n, k)) return PBG_ERR_SHAPE;
+  if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_ternary_gemv(packed, scale, n, k, x, y, stream));
+}
+
+int ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                       int64_t m, float* y, hipStream_t stream) {
+  if (!packed || !scale || !x || !y) return PBG_ERR_NULL;
+  if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_ternary_gemm_small(packed, scale, n, k, x, static_cast<int>(m), y, stream));
+}
+
+int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+                   float* y, hipStream_t stream) {
+  if (!w || !scale || !x || !y) return PBG_ERR_NULL;
+  if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(w, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_int8_head(w, scale, n, k, x, static_cast<int>(m), y, stream));
+}
+
+}  // extern "C"

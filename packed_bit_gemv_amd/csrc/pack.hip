@@ -1,0 +1,100 @@
+// pack_ternary: int8 codes -> 2-bit words, row sums and code counts.
+// Load-time step; the per-row scale and row sum are the row metadata of the
+// Neutrino-1 8B model page ("Where the bytes live"), the counts its code
+// occupancy ("Inside the coded lane").
+#include "pbg_device.hpp"
+#include "pbg_internal.hpp"
+
+namespace pbg {
+namespace {
+
+constexpr int kPackThreads = 256;
+
+// Nonzero and sign bit of code j (0..15) in its word.
+__device__ __forceinline__ uint32_t nz_bit(int j) { return (10u + 16u * (j & 1) + 2u * (j >> 1)) & 31u; }
+__device__ __forceinline__ uint32_t sign_bit(int j) { return (15u + 16u * (j & 1) + 2u * (j >> 1)) & 31u; }
+
+struct Tally {
+  int sum;
+  int minus, zero, plus, invalid;
+};
+
+__device__ __forceinline__ void put_code(int c, int j, uint32_t& word, Tally& t) {
+  if (c == 1) {
+    word |= 1u << nz_bit(j);
+    t.sum += 1;
+    t.plus += 1;
+  } else if (c == -1) {
+    word |= (1u << nz_bit(j)) | (1u << sign_bit(j));
+    t.sum -= 1;
+    t.minus += 1;
+  } else if (c == 0) {
+    t.zero += 1;
+  } else {
+    t.invalid += 1;
+  }
+}
+
+__global__ void zero_stats_kernel(int64_t* stats) {
+  if (threadIdx.x < 4) stats[threadIdx.x] = 0;
+}
+
+// One workgroup per row; thread i packs words i, i + 256, ...
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(const int8_t* __restrict__ codes, int64_t k,
+                                                            int64_t words, uint32_t* __restrict__ packed,
+                                                            int32_t* __restrict__ row_sum,
+                                                            int64_t* __restrict__ stats) {
+  const int64_t row = blockIdx.x;
+  const int8_t* src = codes + row * k;
+  const bool vec = (k % 16 == 0) && ((reinterpret_cast<uintptr_t>(codes) & 15u) == 0);
+  Tally t = {0, 0, 0, 0, 0};
+  for (int64_t w = threadIdx.x; w < words; w += kPackThreads) {
+    uint32_t word = 0;
+    const int64_t c0 = 16 * w;
+    if (c0 < k) {
+      if (vec) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + c0);
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) put_code(static_cast<int8_t>(q[j >> 2] >> (8 * (j & 3))), j, word, t);
+      } else {
+        for (int j = 0; j < 16 && c0 + j < k; ++j) put_code(src[c0 + j], j, word, t);
+      }
+    }
+    packed[row * words + w] = word;
+  }
+  // Workgroup reduction of the tallies (integers: order does not matter).
+  __shared__ int red[5][kPackThreads / kWave];
+  int vals[5] = {t.sum, t.minus, t.zero, t.plus, t.invalid};
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    int v = vals[i];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) red[i][wave] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+      for (int wv = 0; wv < kPackThreads / kWave; ++wv) tot[i] += red[i][wv];
+    row_sum[row] = tot[0];
+    for (int i = 0; i < 4; ++i)
+      if (tot[i + 1]) atomicAdd(reinterpret_cast<unsigned long long*>(stats + i), (unsigned long long)tot[i + 1]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, int32_t* row_sum,
+                       int64_t* stats, hipStream_t stream) {
+  const int64_t words = words_per_row(k);
+  hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, stream, stats);
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(n)), dim3(kPackThreads), 0, stream, codes, k, words,
+                     packed, row_sum, stats);
+  return hipGetLastError();
+}
+
+}  // namespace pbg

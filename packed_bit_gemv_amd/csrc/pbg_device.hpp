@@ -1,0 +1,109 @@
+// Device helpers shared by the gfx950 kernels of libpackedbitgemv.
+//
+// Decoding follows the packed layout declared in include/packed_bit_gemv.h:
+// a word rotated right by 2t and masked with 0x84008400 holds two fp16 values
+// c[2t] * 2^-14 and c[2t+1] * 2^-14 (nonzero flag in the lowest exponent bit,
+// sign in the fp16 sign bit). One v_dot2 then adds or subtracts two fp16
+// activations (or skips them for a zero code) into an fp32 sum; the 2^-14 is
+// folded into the per-row scale. Products c * 2^-14 * x are exact in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pbg {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kPairMask = 0x84008400u;
+constexpr float kCodeUnitInv = 16384.0f;  // 2^14, undoes the 2^-14 of a decoded code
+constexpr int kWave = 64;
+
+__device__ __forceinline__ uint32_t rotr(uint32_t w, uint32_t s) { return __builtin_amdgcn_alignbit(w, w, s); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+// Operand t (0..7) of a word: codes 2t and 2t+1 as fp16 c * 2^-14.
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int t) {
+  return (t == 0 ? w : rotr(w, 2u * t)) & kPairMask;
+}
+
+// Sum over the 16 codes of one word against 8 fp16 activation pairs
+// (xp[t] holds x[2t] in the low half and x[2t+1] in the high half).
+__device__ __forceinline__ float word_dot(uint32_t w, const uint32_t* xp, float acc) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc = dot2(code_pair(w, t), xp[t], acc);
+  return acc;
+}
+
+__device__ __forceinline__ uint32_t as_u32(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float as_f32(uint32_t v) { return __builtin_bit_cast(float, v); }
+
+// DPP row rotate: every lane reads the lane `n` places to its right within its
+// 16-lane row.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return as_f32(__builtin_amdgcn_update_dpp(0u, as_u32(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Sum of a value over the 16 lanes of each row; every lane gets its row's sum.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return v;
+}
+
+// Transposed reduction of four per-lane partial sums over the 64 lanes of a
+// wave. Afterwards lane 0 holds sum(a), lane 32 sum(b), lane 16 sum(c) and
+// lane 48 sum(d). Uses the gfx950 lane swaps: permlane32_swap exchanges lanes
+// 32..63 of its first operand with lanes 0..31 of its second, permlane16_swap
+// exchanges the odd 16-lane rows of the first with the even rows of the
+// second. Needs all 64 lanes active.
+__device__ __forceinline__ float wave_reduce4(float a, float b, float c, float d) {
+  auto ab = __builtin_amdgcn_permlane32_swap(as_u32(a), as_u32(b), false, false);
+  auto cd = __builtin_amdgcn_permlane32_swap(as_u32(c), as_u32(d), false, false);
+  float p = as_f32(ab[0]) + as_f32(ab[1]);  // lanes 0..31: a folded, 32..63: b folded
+  float q = as_f32(cd[0]) + as_f32(cd[1]);  // lanes 0..31: c folded, 32..63: d folded
+  auto pq = __builtin_amdgcn_permlane16_swap(as_u32(p), as_u32(q), false, false);
+  float s = as_f32(pq[0]) + as_f32(pq[1]);  // rows: a, c, b, d (16 lanes each)
+  return row_sum16(s);
+}
+
+// Lane of wave_reduce4's result for operand i (0 = a, 1 = b, 2 = c, 3 = d),
+// and the inverse map (-1 for lanes that hold no result).
+__device__ __forceinline__ int reduce4_slot(int lane) {
+  return lane == 0 ? 0 : lane == 32 ? 1 : lane == 16 ? 2 : lane == 48 ? 3 : -1;
+}
+
+// Loads x[base .. base+2*NPAIR-1] as NPAIR fp16 pairs; columns >= k read 0.
+template <int NPAIR>
+__device__ __forceinline__ void load_x_pairs(const uint16_t* __restrict__ x, int64_t k, int64_t base,
+                                             uint32_t* xp) {
+  static_assert(NPAIR % 4 == 0, "whole 16-byte groups");
+  const uint16_t* p = x + base;
+  if (base + 2 * NPAIR <= k && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < NPAIR / 4; ++i) {
+      uint4 v = q[i];
+      xp[4 * i + 0] = v.x;
+      xp[4 * i + 1] = v.y;
+      xp[4 * i + 2] = v.z;
+      xp[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < NPAIR; ++e) {
+      const int64_t c0 = base + 2 * e;
+      uint32_t lo = c0 < k ? p[2 * e] : 0u;
+      uint32_t hi = c0 + 1 < k ? p[2 * e + 1] : 0u;
+      xp[e] = lo | (hi << 16);
+    }
+  }
+}
+
+}  // namespace pbg

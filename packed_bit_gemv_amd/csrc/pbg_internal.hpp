@@ -1,0 +1,23 @@
+// Host-side launchers behind the C ABI. Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pbg {
+
+hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, int32_t* row_sum,
+                       int64_t* stats, hipStream_t stream);
+
+hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                               const uint16_t* x, float* y, hipStream_t stream);
+
+hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                     const uint16_t* x, int m, float* y, hipStream_t stream);
+
+hipError_t launch_int8_head(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                            int m, float* y, hipStream_t stream);
+
+inline int64_t words_per_row(int64_t k) { return k <= 0 ? 0 : 4 * ((k + 63) / 64); }
+
+}  // namespace pbg

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before any HIP call.
+
+The calls below use fake pointer values that always fail validation; they are
+never made when a GPU is visible, so no kernel can be launched on them.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+from packed_bit_gemv_amd import binding
+
+GOOD = 0x10000  # 64 KiB aligned fake address, never dereferenced
+HOST_GPU = None
+
+
+def _gpu_visible() -> bool:
+    global HOST_GPU
+    if HOST_GPU is None:
+        try:
+            import torch
+
+            HOST_GPU = bool(torch.cuda.is_available())
+        except Exception:
+            HOST_GPU = False
+    return HOST_GPU
+
+
+no_gpu_only = pytest.mark.skipif("_gpu_visible()", reason="fake-pointer calls are only made without a GPU")
+
+
+def test_exports_every_header_function():
+    names = binding.header_functions()
+    assert set(names) >= {"pack_ternary", "ternary_gemv", "ternary_gemm_small", "int8_head_gemv",
+                          "pbg_abi_version", "pbg_strerror", "pbg_words_per_row"}
+    lib = binding.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(binding._SIGNATURES)
+
+
+def test_helpers():
+    lib = binding.lib()
+    assert lib.pbg_abi_version() == 1
+    for k, w in [(1, 4), (64, 4), (65, 8), (4096, 256), (12288, 768), (0, 0), (-5, 0)]:
+        assert lib.pbg_words_per_row(k) == w
+    for code in range(-5, 1):
+        assert lib.pbg_strerror(code)
+    assert lib.pbg_strerror(-99) == b"unknown error code"
+
+
+@no_gpu_only
+def test_null_pointers():
+    lib = binding.lib()
+    assert lib.ternary_gemv(None, GOOD, 4, 64, GOOD, GOOD, None) == -1
+    assert lib.ternary_gemv(GOOD, GOOD, 4, 64, None, GOOD, None) == -1
+    assert lib.ternary_gemm_small(GOOD, None, 4, 64, GOOD, 2, GOOD, None) == -1
+    assert lib.int8_head_gemv(GOOD, GOOD, 4, 64, GOOD, 1, None, None) == -1
+    assert lib.pack_ternary(GOOD, 4, 64, GOOD, GOOD, None, None, None) == -1
+
+
+@no_gpu_only
+@pytest.mark.parametrize("n,k,m", [(0, 64, 1), (4, 0, 1), (-1, 64, 1), (4, 64, 0), (4, 64, 9),
+                                   (2 ** 24 + 1, 64, 1), (4, 2 ** 24 + 1, 1)])
+def test_bad_shapes(n, k, m):
+    lib = binding.lib()
+    assert lib.ternary_gemm_small(GOOD, GOOD, n, k, GOOD, m, GOOD, None) == -2
+    assert lib.int8_head_gemv(GOOD, GOOD, n, k, GOOD, m, GOOD, None) == -2
+    if m == 1:
+        assert lib.ternary_gemv(GOOD, GOOD, n, k, GOOD, GOOD, None) == -2
+        assert lib.pack_ternary(GOOD, n, k, GOOD, GOOD, GOOD, None, None) == -2
+
+
+@no_gpu_only
+def test_misaligned():
+    lib = binding.lib()
+    assert lib.ternary_gemv(GOOD + 4, GOOD, 4, 64, GOOD, GOOD, None) == -3
+    assert lib.ternary_gemv(GOOD, GOOD + 2, 4, 64, GOOD, GOOD, None) == -3
+    assert lib.ternary_gemv(GOOD, GOOD, 4, 64, GOOD + 1, GOOD, None) == -3
+    assert lib.ternary_gemv(GOOD, GOOD, 4, 64, GOOD, GOOD + 2, None) == -3
+    assert lib.int8_head_gemv(GOOD + 8, GOOD, 4, 64, GOOD, 1, GOOD, None) == -3
+    assert lib.ternary_gemm_small(GOOD + 8, GOOD, 4, 64, GOOD, 2, GOOD, None) == -3
+    assert lib.pack_ternary(GOOD, 4, 64, GOOD + 4, GOOD, GOOD, None, None) == -3
+    assert lib.pack_ternary(GOOD, 4, 64, GOOD, GOOD, GOOD + 4, None, None) == -3
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        binding.ternary_gemv(torch.zeros((4, 4), dtype=torch.int32), torch.zeros(4), 64,
+                             torch.zeros(64, dtype=torch.float16))
+
+
+def test_strerror_is_static():
+    lib = binding.lib()
+    a = ctypes.cast(lib.pbg_strerror(-1), ctypes.c_char_p)
+    assert a.value == b"a required pointer is NULL"

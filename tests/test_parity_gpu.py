@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer and byte work is compared bit for bit (packed words, row sums, code
+counts). Floating-point outputs are compared
+  * bit for bit on exact-arithmetic probes (integer activations, power-of-two
+    scales: every fp32 partial sum is an exact integer multiple of 2^-14, so
+    any summation order gives the oracle's value), which catches any single
+    wrong code, sign or index;
+  * within |y - y_ref| <= 1e-3 * s_r * sum_j |x_j| (ternary) or
+    1e-3 * s_v * sum_j |w_vj| |x_j| (head) on the seeded workloads.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_within, head_bound, ternary_bound
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def pbg(gpu):
+    import packed_bit_gemv_amd as m
+
+    m.lib()
+    return m
+
+
+def dev(a: np.ndarray, device="cuda:0"):
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def host_words(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def gpu_pack(pbg, codes: np.ndarray):
+    packed, row_sum, stats = pbg.pack_ternary(dev(codes))
+    return packed, row_sum, stats
+
+
+SHAPES_SMALL = [(1, 1), (3, 7), (5, 16), (4, 64), (17, 65), (9, 100), (33, 1000), (40, 4096), (50, 4097),
+                (21, 8200), (64, 12288), (7, 20000)]
+
+
+# --------------------------------------------------------------------------
+# pack_ternary
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,k", SHAPES_SMALL + [(1024, 4096)])
+def test_pack_bit_exact(pbg, n, k):
+    say(f"pack n={n} k={k}")
+    codes = synth.ternary_codes(1000 + n + k, n, k)
+    ref_p, ref_rs, ref_c = oracle.pack(codes)
+    p, rs, st = gpu_pack(pbg, codes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_words(p), ref_p)
+    assert np.array_equal(rs.cpu().numpy(), ref_rs)
+    assert st.cpu().numpy().tolist() == ref_c.tolist() + [0]
+
+
+def test_pack_gate_full(pbg):
+    say("pack gate 12288x4096")
+    codes = synth.ternary_codes(synth.tensor_seed(1, "gate"), 12288, 4096, synth.code_dist(1, "gate"))
+    ref_p, ref_rs, ref_c = oracle.pack(codes)
+    p, rs, st = gpu_pack(pbg, codes)
+    assert np.array_equal(host_words(p), ref_p)
+    assert np.array_equal(rs.cpu().numpy(), ref_rs)
+    assert st.cpu().numpy().tolist() == ref_c.tolist() + [0]
+
+
+def test_pack_unaligned_source(pbg):
+    """Codes starting at an odd address take the byte-wise path."""
+    n, k = 6, 160
+    codes = synth.ternary_codes(77, n, k)
+    buf = torch.zeros(n * k + 1, dtype=torch.int8, device="cuda:0")
+    buf[1:] = dev(codes.reshape(-1))
+    view = buf[1:].view(n, k)
+    p, rs, st = pbg.pack_ternary(view)
+    ref_p, ref_rs, ref_c = oracle.pack(codes)
+    assert np.array_equal(host_words(p), ref_p)
+    assert np.array_equal(rs.cpu().numpy(), ref_rs)
+
+
+def test_pack_invalid_codes(pbg):
+    codes = synth.ternary_codes(78, 8, 300)
+    codes[2, 5] = 2
+    codes[7, 299] = -128
+    with pytest.raises(pbg.PbgError) as e:
+        gpu_pack(pbg, codes)
+    assert e.value.code == -4
+    _, _, st = pbg.pack_ternary(dev(codes), check=False)
+    assert st.cpu().numpy()[3] == 2
+
+
+# --------------------------------------------------------------------------
+# ternary_gemv (M = 1)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,k", SHAPES_SMALL)
+def test_gemv_exact_probe(pbg, n, k):
+    say(f"gemv exact n={n} k={k}")
+    codes = synth.ternary_codes(2000 + n + k, n, k)
+    x = synth.probe_activations(3000 + k, 1, k)[0]
+    s = synth.pow2_scales(4000 + n, n)
+    ref = oracle.ternary_gemv(oracle.pack(codes)[0], s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    y = pbg.ternary_gemv(p, dev(s), k, dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("n,k", SHAPES_SMALL)
+def test_gemv_random_tolerance(pbg, n, k):
+    say(f"gemv random n={n} k={k}")
+    codes = synth.ternary_codes(5000 + n + k, n, k)
+    x = synth.activations(6000 + k, 1, k)[0]
+    s = synth.row_scales(7000 + n, n)
+    ref = oracle.ternary_gemv(oracle.pack(codes)[0], s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    y = pbg.ternary_gemv(p, dev(s), k, dev(x)).cpu().numpy()
+    assert_within(y[None], ref[None], ternary_bound(s, x), f"gemv {n}x{k}")
+
+
+@pytest.mark.parametrize("proj", ["k", "q", "gate", "up", "down"])
+def test_gemv_config_shapes(pbg, proj):
+    """Full config shapes at M = 1 (seeded as in the benchmark's numpy recipe)."""
+    n, k = synth.SHAPES[proj]
+    layer = 1
+    say(f"gemv config {proj} {n}x{k}")
+    codes = synth.ternary_codes(synth.tensor_seed(layer, proj), n, k, synth.code_dist(layer, proj))
+    s = synth.row_scales(synth.tensor_seed(layer, proj), n)
+    x = synth.activations(synth.x_seed(0), 1, k)[0]
+    ref = oracle.ternary_gemv(oracle.pack(codes)[0], s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    y = pbg.ternary_gemv(p, dev(s), k, dev(x)).cpu().numpy()
+    assert_within(y[None], ref[None], ternary_bound(s, x), f"{proj}")
+    # bitwise repeatable
+    y2 = pbg.ternary_gemv(p, dev(s), k, dev(x)).cpu().numpy()
+    assert np.array_equal(y, y2)
+
+
+def test_gemv_special_cases(pbg):
+    n = k = 300
+    x = synth.activations(11, 1, k)[0]
+    s = synth.row_scales(12, n)
+    xd, sd = dev(x), dev(s)
+    zero = np.zeros((n, k), dtype=np.int8)
+    y0 = pbg.ternary_gemv(gpu_pack(pbg, zero)[0], sd, k, xd).cpu().numpy()
+    assert np.all(y0 == 0.0)
+    eye = np.eye(n, k, dtype=np.int8)
+    ye = pbg.ternary_gemv(gpu_pack(pbg, eye)[0], sd, k, xd).cpu().numpy()
+    assert np.array_equal(ye.astype(np.float64), (s.astype(np.float64) * x.astype(np.float64)).astype(np.float32))
+    codes = synth.ternary_codes(13, n, k)
+    y = pbg.ternary_gemv(gpu_pack(pbg, codes)[0], sd, k, xd).cpu().numpy()
+    yn = pbg.ternary_gemv(gpu_pack(pbg, -codes)[0], sd, k, xd).cpu().numpy()
+    assert np.array_equal(yn, -y)
+
+
+def test_gemv_full_size_sampled(pbg):
+    """Device-generated gate and down tensors at full size (the benchmark's
+    generator), checked on sampled rows against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    for proj, layer in (("gate", 2), ("down", 2), ("up", 5)):
+        n, k = synth.SHAPES[proj]
+        say(f"gemv full-size sampled {proj}")
+        codes = synth.ternary_codes_device(synth.tensor_seed(layer, proj), n, k, synth.code_dist(layer, proj),
+                                           "cuda:0")
+        s = synth.row_scales_device(synth.tensor_seed(layer, proj), n, "cuda:0")
+        x = synth.activations(synth.x_seed(0), 1, k)[0]
+        p, _, st = pbg.pack_ternary(codes)
+        y = pbg.ternary_gemv(p, s, k, dev(x)).cpu().numpy()
+        rows = np.sort(rng.choice(n, size=256, replace=False))
+        c_rows = codes[torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
+        s_rows = s.cpu().numpy()[rows]
+        ref = oracle.ternary_gemv(oracle.pack(c_rows)[0], s_rows, k, x)
+        assert_within(y[rows][None], ref[None], ternary_bound(s_rows, x), proj)
+        assert np.array_equal(host_words(p)[rows], oracle.pack(c_rows)[0])
+
+
+# --------------------------------------------------------------------------
+# ternary_gemm_small (M <= 8)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("n,k", [(5, 16), (17, 65), (40, 4096), (21, 8200), (64, 12288)])
+def test_small_m_exact_probe(pbg, m, n, k):
+    say(f"small-m exact m={m} n={n} k={k}")
+    codes = synth.ternary_codes(8000 + n + k, n, k)
+    x = synth.probe_activations(9000 + m, m, k)
+    s = synth.pow2_scales(9100 + n, n)
+    ref = oracle.ternary_gemm_small(oracle.pack(codes)[0], s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    y = pbg.ternary_gemm_small(p, dev(s), k, dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("m", [2, 4, 7, 8])
+@pytest.mark.parametrize("proj", ["k", "o", "gate", "down"])
+def test_small_m_config_shapes(pbg, m, proj):
+    n, k = synth.SHAPES[proj]
+    say(f"small-m config m={m} {proj}")
+    codes = synth.ternary_codes(synth.tensor_seed(0, proj), n, k, synth.code_dist(0, proj))
+    s = synth.row_scales(synth.tensor_seed(0, proj), n)
+    x = synth.activations(synth.x_seed(0), m, k)
+    ref = oracle.ternary_gemm_small(oracle.pack(codes)[0], s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    y = pbg.ternary_gemm_small(p, dev(s), k, dev(x)).cpu().numpy()
+    assert_within(y, ref, ternary_bound(s, x), f"{proj} m={m}")
+
+
+# --------------------------------------------------------------------------
+# int8_head_gemv
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("n,k", [(1, 16), (3, 5), (17, 100), (40, 4096), (33, 4112), (9, 12288)])
+def test_head_exact_probe(pbg, m, n, k):
+    say(f"head exact m={m} n={n} k={k}")
+    w = synth.int8_full_range(10000 + n + k, n, k)
+    x = synth.probe_activations(11000 + m, m, k)
+    s = synth.pow2_scales(12000 + n, n)
+    ref = oracle.int8_head_gemv(w, s, x)
+    y = pbg.int8_head_gemv(dev(w), dev(s), dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 7, 8])
+def test_head_random_tolerance(pbg, m):
+    n, k = 4099, 4096
+    say(f"head random m={m}")
+    w = synth.head_weights(13000, n, k)
+    x = synth.activations(14000 + m, m, k)
+    s = synth.row_scales(15000, n)
+    ref = oracle.int8_head_gemv(w, s, x)
+    y = pbg.int8_head_gemv(dev(w), dev(s), dev(x)).cpu().numpy()
+    assert_within(y, ref, head_bound(w, s, x), f"head m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_head_full_size_sampled(pbg, m):
+    n, k = synth.HEAD_SHAPE
+    say(f"head full-size sampled m={m}")
+    w = synth.head_weights_device(synth.SEED_HEAD, n, k, "cuda:0")
+    s = synth.row_scales_device(synth.SEED_HEAD, n, "cuda:0")
+    x = synth.activations(synth.x_seed(0), m, k)
+    y = pbg.int8_head_gemv(w, s, dev(x)).cpu().numpy()
+    rows = np.sort(np.random.Generator(np.random.PCG64(9)).choice(n, size=512, replace=False))
+    rows = np.concatenate([rows, [0, n - 1]])
+    w_rows = w[torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
+    s_rows = s.cpu().numpy()[rows]
+    ref = oracle.int8_head_gemv(w_rows, s_rows, x)
+    assert_within(y[:, rows], ref, head_bound(w_rows, s_rows, x), "head full")
+
+
+# --------------------------------------------------------------------------
+# Error paths with real device buffers
+# --------------------------------------------------------------------------
+def test_device_error_paths(pbg):
+    lib = pbg.lib()
+    p = torch.zeros((8, 4), dtype=torch.int32, device="cuda:0")
+    s = torch.ones(8, dtype=torch.float32, device="cuda:0")
+    x = torch.ones(64, dtype=torch.float16, device="cuda:0")
+    y = torch.empty(8, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    assert lib.ternary_gemv(p.data_ptr() + 4, s.data_ptr(), 7, 64, x.data_ptr(), y.data_ptr(), stream) == -3
+    assert lib.ternary_gemv(p.data_ptr(), s.data_ptr(), 8, 0, x.data_ptr(), y.data_ptr(), stream) == -2
+    assert lib.ternary_gemm_small(p.data_ptr(), s.data_ptr(), 8, 64, x.data_ptr(), 9, y.data_ptr(), stream) == -2
+    assert lib.ternary_gemv(p.data_ptr(), s.data_ptr(), 8, 64, x.data_ptr(), y.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
