@@ -32,6 +32,7 @@ import synth  # noqa: E402
 METRIC = "achieved HBM GB/s (% of peak) for packed-ternary GEMV, M=1; µs per decoder layer"
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_ternary_gemv_ffn_m1.json")
+CHUNK = 12  # steps per replayed graph in the timed region
 KERNEL_SOURCES = ("packed_bit_gemv_amd/csrc/ternary.hip", "packed_bit_gemv_amd/csrc/pbg_device.hpp")
 
 
@@ -80,16 +81,31 @@ class Model:
         torch.cuda.synchronize()
 
 
-def time_region(torch, fn, steps: int, warmup: int):
-    """Runs fn(i) warmup times, then times exactly `steps` calls; ms per step."""
+def capture(torch, fn):
+    """Captures fn() into a HIP graph (fn launches on the current stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, steps: int, warmup: int):
+    """Replays graphs[i % len] warmup times, then times exactly `steps` replays; ms per replay."""
     for i in range(warmup):
-        fn(i)
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        fn(warmup + i)
+        graphs[(warmup + i) % len(graphs)].replay()
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
@@ -172,38 +188,53 @@ def main():
         else:
             pbg.ternary_gemm_small(packed, s, k, xs[k][:m], ys[p][:m])
 
-    def ffn_step(i):
+    def ffn_step(layer):
         for p in ffn:
-            linear(i % L, p)
-
-    # ---- headline: FFN GEMVs at M = 1, timed region ------------------------
-    bytes_step = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)
-    for i in range(args.warmup):
-        ffn_step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * 3 * args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    j = 0
-    for i in range(args.steps):
-        layer = (args.warmup + i) % L
-        for p in ffn:
-            ev[j].record(stream)
             linear(layer, p)
-            ev[j + 1].record(stream)
-            j += 2
-    end.record(stream)
+
+    # ---- headline: FFN GEMVs at M = 1 ---------------------------------------
+    # Steps are replayed from HIP graphs: step i runs the gate, up and down
+    # GEMVs of layer i % L, so consecutive steps stream different weights from
+    # HBM. Runs of CHUNK steps that start at a multiple of CHUNK replay one
+    # graph of 3 * CHUNK launches; other steps replay a one-step graph, so
+    # exactly `steps` steps are timed. Events on the replay stream bracket the
+    # timed region.
+    chunk = CHUNK if L % CHUNK == 0 else 1
+    single = [capture(torch, lambda l=l: ffn_step(l)) for l in range(L)]
+    chunked = [capture(torch, lambda c=c: [ffn_step(c * chunk + j) for j in range(chunk)])
+               for c in range(L // chunk)]
+
+    def replay_steps(first, count):
+        i = first
+        while i < first + count:
+            if chunk > 1 and i % chunk == 0 and i + chunk <= first + count:
+                chunked[(i % L) // chunk].replay()
+                i += chunk
+            else:
+                single[i % L].replay()
+                i += 1
+
+    bytes_step = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)
+    replay_steps(0, args.warmup)
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    launch_ms = np.array([ev[2 * q].elapsed_time(ev[2 * q + 1]) for q in range(3 * args.steps)])
-    per_proj_us = {p: float(np.mean(launch_ms[i::3]) * 1e3) for i, p in enumerate(ffn)}
-    avg_launch_us = float(launch_ms.mean() * 1e3)
-    achieved = bytes_step / 3 / (avg_launch_us * 1e-6) / 1e9
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
+    ev_start.record()
+    replay_steps(args.warmup, args.steps)
+    ev_end.record()
+    torch.cuda.synchronize()
+    ms_step = ev_start.elapsed_time(ev_end) / args.steps
     value = bytes_step / (ms_step * 1e-3) / 1e9
-    log(f"ffn step {ms_step * 1e3:.2f} us, {value:.1f} GB/s; per launch {per_proj_us}")
+    avg_launch_us = ms_step * 1e3 / len(ffn)
+    achieved = bytes_step / len(ffn) / (avg_launch_us * 1e-6) / 1e9
+    log(f"ffn step {ms_step * 1e3:.3f} us, {value:.1f} GB/s; {avg_launch_us:.3f} us per launch")
+    del single, chunked
+
+    # per-projection launch time: a graph of the same projection over all layers
+    per_proj_us = {}
+    for p in ffn:
+        g = capture(torch, lambda p=p: [linear(l, p) for l in range(L)])
+        per_proj_us[p] = time_graphs(torch, [g], 5, 1) * 1e3 / L
 
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
@@ -212,26 +243,30 @@ def main():
         if tr.get("kernel_hash") == kernel_hash():
             traffic = tr.get("bytes_per_launch")
 
-    extra = {"us_per_launch_event": {p: round(v, 3) for p, v in per_proj_us.items()},
+    extra = {"us_per_launch": {p: round(v, 3) for p, v in per_proj_us.items()},
+             "GBs_per_launch": {p: round(ternary_bytes(*synth.SHAPES[p]) / (v * 1e-6) / 1e9, 1)
+                                for p, v in per_proj_us.items()},
              "layers_in_pool": L, "pool_bytes_packed": bytes_step * L}
 
     if not args.no_extra:
         K, W = max(20, args.steps // 4), 5
-        # per-linear (M = 1), walking the layer pool
-        for p in synth.PROJECTIONS:
-            ms = time_region(torch, lambda i, p=p: linear(i % L, p), K, W)
-            n, k = synth.SHAPES[p]
-            extra[f"{p}_m1_us"] = round(ms * 1e3, 3)
-            extra[f"{p}_m1_GBs"] = round(ternary_bytes(n, k) / (ms * 1e-3) / 1e9, 1)
-
-        def layer_step(i, m=1):
-            for p in synth.PROJECTIONS:
-                linear(i % L, p, m)
-
-        ms = time_region(torch, layer_step, K, W)
         layer_bytes = sum(ternary_bytes(*synth.SHAPES[p]) for p in synth.PROJECTIONS)
+        for p in ("q", "k", "v", "o"):
+            g = capture(torch, lambda p=p: [linear(l, p) for l in range(L)])
+            us = time_graphs(torch, [g], 5, 1) * 1e3 / L
+            n, k = synth.SHAPES[p]
+            extra["us_per_launch"][p] = round(us, 3)
+            extra["GBs_per_launch"][p] = round(ternary_bytes(n, k) / (us * 1e-6) / 1e9, 1)
+
+        def layer_step(layer, m=1):
+            for p in synth.PROJECTIONS:
+                linear(layer, p, m)
+
+        layer_graphs = [capture(torch, lambda l=l: layer_step(l)) for l in range(L)]
+        ms = time_graphs(torch, layer_graphs, K, W)
         extra["layer_m1_us"] = round(ms * 1e3, 3)
         extra["layer_m1_GBs"] = round(layer_bytes / (ms * 1e-3) / 1e9, 1)
+        del layer_graphs
 
         hw, hs, hn, hk = model.head
         yh = torch.empty((8, hn), dtype=torch.float32, device=device)
@@ -240,35 +275,40 @@ def main():
             pbg.int8_head_gemv(hw, hs, xs[hk][:m], yh[:m])
 
         for m in (1, 2, 4, 7, 8):
-            ms = time_region(torch, lambda i, m=m: head(m), 10, 2)
+            g = capture(torch, lambda m=m: head(m))
+            ms = time_graphs(torch, [g], 10, 2)
             extra[f"head_m{m}_us"] = round(ms * 1e3, 2)
             extra[f"head_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
 
-        def decode_step(i):
+        def decode_step():
             for l in range(L):
-                for p in synth.PROJECTIONS:
-                    linear(l, p)
+                layer_step(l)
             head(1)
 
-        ms = time_region(torch, decode_step, 5, 1)
+        g = capture(torch, decode_step)
+        ms = time_graphs(torch, [g], 5, 1)
         dec_bytes = layer_bytes * L + head_bytes(hn, hk)
         extra["decode_step_m1_us"] = round(ms * 1e3, 1)
         extra["decode_step_m1_GBs"] = round(dec_bytes / (ms * 1e-3) / 1e9, 1)
+        del g
 
         for m in (2, 4, 7, 8):
-            ms = time_region(torch, lambda i, m=m: layer_step(i, m), K, W)
+            graphs = [capture(torch, lambda l=l, m=m: layer_step(l, m)) for l in range(L)]
+            ms = time_graphs(torch, graphs, K, W)
             lb = sum(ternary_bytes(*synth.SHAPES[p], m) for p in synth.PROJECTIONS)
             extra[f"layer_m{m}_us"] = round(ms * 1e3, 3)
             extra[f"layer_m{m}_GBs"] = round(lb / (ms * 1e-3) / 1e9, 1)
+            del graphs
 
-        # streaming-read ceiling at the FFN byte count: torch copy of a pool
+        # streaming-read ceiling at the gate byte count: torch copy over a pool
         nbytes = synth.words_bytes(*synth.SHAPES["gate"])
         pool = [torch.empty(nbytes // 4, dtype=torch.int32, device=device) for _ in range(48)]
         dst = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
-        ms = time_region(torch, lambda i: dst.copy_(pool[i % 48]), 60, 10)
+        g = capture(torch, lambda: [dst.copy_(pool[i]) for i in range(48)])
+        ms = time_graphs(torch, [g], 5, 1) / 48
         extra["copy_12.6MB_us"] = round(ms * 1e3, 3)
         extra["copy_12.6MB_GBs_read_plus_write"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
-        del pool, dst
+        del pool, dst, g
 
     result = {
         "metric": METRIC,
@@ -299,6 +339,7 @@ def main():
             "traffic": traffic,
             "kernel": "ternary_gemv_kernel",
             "avg_launch_us": round(avg_launch_us, 3),
+            "launch_us_note": "timed-region time / launches; HIP graphs of 12 steps (36 launches), gaps included",
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
         "extra": extra,

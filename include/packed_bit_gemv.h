@@ -16,11 +16,13 @@
  * Packed layout (this library's own; the page calls its format proprietary):
  *   - 2 bits per code, 16 codes per little-endian uint32 word;
  *   - code j (0..15) of a word: pair t = j / 2, half h = j % 2;
- *       nonzero bit at (10 + 16*h + 2*t) mod 32,
- *       sign bit    at (15 + 16*h + 2*t) mod 32;
- *     +1 = (nonzero 1, sign 0), -1 = (1, 1), 0 = (0, 0); (0, 1) never occurs.
- *     Rotating a word right by 2t and masking with 0x84008400 leaves two
- *     IEEE fp16 values equal to c[2t] * 2^-14 and c[2t+1] * 2^-14.
+ *       nonzero bit at 16*h + 14 - 2*t,
+ *       sign bit    at 16*h + 15 - 2*t;
+ *     so each 16-bit half holds 8 two-bit fields, highest first (even codes
+ *     in the low half, odd codes in the high half), and a field read as a
+ *     2-bit two's-complement integer is the code: +1 = 01, -1 = 11, 0 = 00;
+ *     10 never occurs. Shifting a word left by 2t and masking with
+ *     0xC000C000 leaves two IEEE fp16 values equal to 2*c[2t], 2*c[2t+1].
  *   - row r of an N x K matrix is pbg_words_per_row(K) = 4 * ceil(K / 64)
  *     consecutive words (a whole number of 16-byte chunks); word w holds the
  *     codes of columns 16w .. 16w+15; codes past column K-1 are 0.

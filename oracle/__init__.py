@@ -22,10 +22,13 @@ What it computes (Neutrino-1 8B model page, English text on bittide):
 
 Bit layout of one 32-bit word (little-endian uint32) holding 16 codes:
   code j (0..15) belongs to pair t = j // 2 and half h = j % 2;
-  its NONZERO bit is bit (10 + 16*h + 2*t) mod 32,
-  its SIGN bit    is bit (15 + 16*h + 2*t) mod 32;
+  its NONZERO bit is bit 16*h + 14 - 2*t,
+  its SIGN bit    is bit 16*h + 15 - 2*t;
+  i.e. each 16-bit half holds 8 two-bit fields, highest field first (even
+  codes in the low half, odd codes in the high half), and a field read as a
+  2-bit two's-complement integer is the code:
   +1 -> nonzero=1, sign=0;  -1 -> nonzero=1, sign=1;  0 -> both bits 0.
-  The pattern sign=1, nonzero=0 is never written; unpacking rejects it.
+  The pattern sign=1, nonzero=0 (-2) is never written; unpacking rejects it.
 Row layout: row r holds W = 4 * ceil(K / 64) words; word w holds the codes of
 columns 16*w .. 16*w + 15; codes past column K - 1 are 0 (row padding, so a
 row is a whole number of 16-byte chunks).
@@ -38,7 +41,7 @@ integer multiple of 2**-24 below 2**53 * 2**-24 and the fp64 sum is exact in
 any order; the only rounding is the final multiply by the scale.
 
 Parity pins: see tests/test_oracle.py (exhaustive single-word round trip,
-hand-written format words, the fp16 decode property of the layout, brute force
+hand-written format words, the fp16 reading of the layout, brute force
 over all ternary rows for K <= 8 against exact rational sums, closed forms,
 exact integer matmul for the head, the row-sum and count invariants).
 """
@@ -63,7 +66,7 @@ def bit_positions(j: int) -> tuple[int, int]:
     if not 0 <= j < CODES_PER_WORD:
         raise ValueError("code index within a word is 0..15")
     t, h = divmod(j, 2)
-    return (10 + 16 * h + 2 * t) % 32, (15 + 16 * h + 2 * t) % 32
+    return 16 * h + 14 - 2 * t, 16 * h + 15 - 2 * t
 
 
 def count_codes(codes: np.ndarray) -> np.ndarray:

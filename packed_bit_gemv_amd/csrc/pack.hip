@@ -11,8 +11,8 @@ namespace {
 constexpr int kPackThreads = 256;
 
 // Nonzero and sign bit of code j (0..15) in its word.
-__device__ __forceinline__ uint32_t nz_bit(int j) { return (10u + 16u * (j & 1) + 2u * (j >> 1)) & 31u; }
-__device__ __forceinline__ uint32_t sign_bit(int j) { return (15u + 16u * (j & 1) + 2u * (j >> 1)) & 31u; }
+__device__ __forceinline__ uint32_t nz_bit(int j) { return 16u * (j & 1) + 14u - 2u * (j >> 1); }
+__device__ __forceinline__ uint32_t sign_bit(int j) { return nz_bit(j) + 1u; }
 
 struct Tally {
   int sum;

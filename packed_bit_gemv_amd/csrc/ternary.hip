@@ -5,51 +5,196 @@
 // kernels, introduction; per-row scale, "Where the bytes live"; a drafted run
 // scored in one forward pass, "speculative").
 //
-// Work split: a wave owns 4 consecutive rows. Lane l streams 16-byte chunks
-// l, l+64, ... of each row (one wave-wide 1 KiB load per row per 4,096
-// columns), keeps the matching 64 activations in registers as fp16 pairs and
-// accumulates fp32 partial sums with v_dot2. The four row sums are finished
-// by one transposed cross-lane reduction.
+// Work split (M = 1): a wave owns R consecutive rows and one 4,096-column
+// K-slice of them. Lane l streams 16-byte chunks (64 codes) of each row, keeps
+// the 64 matching activations in registers as fp16 pairs and accumulates fp32
+// partial sums with v_dot2; every row load of the wave is in flight before the
+// first decode. Rows are finished four at a time by a transposed cross-lane
+// reduction; K-slices of one row meet in LDS.
 #include "pbg_device.hpp"
 #include "pbg_internal.hpp"
 
 namespace pbg {
 namespace {
 
-constexpr int kRowsPerWave = 4;
+constexpr int kRowsPerWave = 4;  // small-M kernel
 constexpr int kGemvWaves = 4;
 
 // Sum over one 16-byte chunk (4 words, 64 codes) against 32 activation pairs.
+// The four words feed four independent accumulators, interleaved so that a
+// single wave per SIMD still keeps the dot unit busy.
 __device__ __forceinline__ float chunk_dot(const uint4& w, const uint32_t* xp, float acc) {
-  float a0 = word_dot(w.x, xp + 0, 0.0f);
-  float a1 = word_dot(w.y, xp + 8, 0.0f);
-  float a2 = word_dot(w.z, xp + 16, 0.0f);
-  float a3 = word_dot(w.w, xp + 24, 0.0f);
+  uint32_t op[4][8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    op[0][t] = code_pair(w.x, t);
+    op[1][t] = code_pair(w.y, t);
+    op[2][t] = code_pair(w.z, t);
+    op[3][t] = code_pair(w.w, t);
+  }
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    a0 = dot2(op[0][t], xp[t], a0);
+    a1 = dot2(op[1][t], xp[8 + t], a1);
+    a2 = dot2(op[2][t], xp[16 + t], a2);
+    a3 = dot2(op[3][t], xp[24 + t], a3);
+  }
   return acc + ((a0 + a1) + (a2 + a3));
 }
 
-__global__ __launch_bounds__(kGemvWaves* kWave) void ternary_gemv_kernel(const uint4* __restrict__ packed,
-                                                                          const float* __restrict__ scale,
-                                                                          int64_t n, int64_t k, int64_t chunks,
-                                                                          const uint16_t* __restrict__ x,
-                                                                          float* __restrict__ y) {
+// M = 1, fast path: k % 8 == 0, x 16-byte aligned and at most 4 K-slices of
+// 4,096 columns (one per wave of a row group). A workgroup holds G row
+// groups x SW K-slices; wave (g, s) owns R consecutive rows and the 16-byte
+// chunk s*64 + lane of each of them.
+//  1. Every thread loads its share of the workgroup's activations, then a
+//     barrier: all activation loads are queued in the vector memory pipe
+//     before any weight load, so they return first.
+//  2. Each wave issues all R row loads (rows past n clamped to n-1) and the
+//     row scales, unconditionally, so the compiler can retire them one row
+//     at a time.
+//  3. The activations go through LDS (q-major, conflict-free reads) into 32
+//     fp16 pairs per lane, and the rows are decoded as they arrive.
+//  4. Rows are reduced four at a time across the wave; with SW > 1 the
+//     per-slice sums meet in LDS and are added in slice order.
+template <int SW, int G, int R>
+__global__ __launch_bounds__(SW* G* kWave) void ternary_gemv_kernel(const uint4* __restrict__ packed,
+                                                                     const float* __restrict__ scale, int64_t n,
+                                                                     int64_t k, int64_t chunks,
+                                                                     const uint16_t* x,  // not restrict: keeps
+                                                                     float* __restrict__ y) {  // its loads above the barrier
+  constexpr int kThreads = SW * G * kWave;
+  constexpr int kChunks = SW * kWave;        // 16-byte weight chunks per row in this workgroup
+  constexpr int kGroups = kChunks * 8;       // groups of 8 activations
+  constexpr int kXPer = (kGroups + kThreads - 1) / kThreads;
+  constexpr int kRed = (R + 3) / 4;
+  __shared__ uint4 xs[kGroups];              // group (c, q) at q * kChunks + c
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kGemvWaves + (threadIdx.x / kWave)) * kRowsPerWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = wave / SW, s = wave % SW;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * G + g) * R;
+  const int64_t groups = k / 8;
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+
+  // 1. activations first
+  uint4 xv[kXPer];
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int gi = threadIdx.x + i * kThreads;
+    xv[i] = xg[gi < groups ? gi : 0];
+  }
+  // Order, not wait: the activation loads stay in flight across the barrier.
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. rows and scales
+  const int64_t c = static_cast<int64_t>(s) * kWave + lane;
+  const int64_t cc = c < chunks ? c : chunks - 1;
+  uint4 w[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) w[i] = packed[(row0 + i < n ? row0 + i : n - 1) * chunks + cc];
+  const int slot = reduce4_slot(lane);
+  float sc[kRed];
+#pragma unroll
+  for (int q = 0; q < kRed; ++q) {
+    const int64_t r = row0 + 4 * q + (slot < 0 ? 0 : slot);
+    sc[q] = scale[r < n ? r : n - 1];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. activations through LDS into registers
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int gi = threadIdx.x + i * kThreads;
+    if (gi < kGroups) {
+      const uint4 v = gi < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);  // zero past k
+      xs[(gi & 7) * kChunks + (gi >> 3)] = v;
+    }
+  }
+  __syncthreads();
+  uint32_t xp[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = xs[q * kChunks + s * kWave + lane];
+    xp[4 * q + 0] = v.x;
+    xp[4 * q + 1] = v.y;
+    xp[4 * q + 2] = v.z;
+    xp[4 * q + 3] = v.w;
+  }
+  float acc[4 * kRed];
+#pragma unroll
+  for (int i = 0; i < 4 * kRed; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) acc[i] = chunk_dot(w[i], xp, 0.0f);
+
+  // 4. reduction and epilogue
+  float red[kRed];
+#pragma unroll
+  for (int q = 0; q < kRed; ++q) red[q] = wave_reduce4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  if constexpr (SW == 1) {
+    if (slot >= 0) {
+#pragma unroll
+      for (int q = 0; q < kRed; ++q) {
+        const int64_t r = row0 + 4 * q + slot;
+        if (4 * q + slot < R && r < n) y[r] = red[q] * (sc[q] * kCodeUnitInv);
+      }
+    }
+  } else {
+    __shared__ float part[G][SW][4 * kRed];
+    if (slot >= 0) {
+#pragma unroll
+      for (int q = 0; q < kRed; ++q) part[g][s][4 * q + slot] = red[q] * kCodeUnitInv;
+    }
+    __syncthreads();
+    if (s == 0 && slot >= 0) {
+#pragma unroll
+      for (int q = 0; q < kRed; ++q) {
+        const int64_t r = row0 + 4 * q + slot;
+        if (4 * q + slot < R && r < n) {
+          float sum = part[g][0][4 * q + slot];
+#pragma unroll
+          for (int t = 1; t < SW; ++t) sum += part[g][t][4 * q + slot];
+          y[r] = sum * sc[q];
+        }
+      }
+    }
+  }
+}
+
+// M = 1, any k and any 2-byte-aligned x: a wave owns 4 rows, loads are
+// guarded element by element. Used only when the fast path's layout
+// conditions do not hold.
+__global__ __launch_bounds__(4 * kWave) void ternary_gemv_generic_kernel(const uint4* __restrict__ packed,
+                                                                         const float* __restrict__ scale,
+                                                                         int64_t n, int64_t k, int64_t chunks,
+                                                                         const uint16_t* __restrict__ x,
+                                                                         float* __restrict__ y) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x / kWave)) * 4;
   if (row0 >= n) return;  // whole wave leaves together
-  float acc[kRowsPerWave] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t c = lane; c < chunks; c += kWave) {
     uint32_t xp[32];
     load_x_pairs<32>(x, k, 64 * c, xp);
-    uint4 w[kRowsPerWave];
+    uint4 w[4];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i)
-      w[i] = (row0 + i < n) ? packed[(row0 + i) * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 4; ++i) w[i] = (row0 + i < n) ? packed[(row0 + i) * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) acc[i] = chunk_dot(w[i], xp, acc[i]);
+    for (int i = 0; i < 4; ++i) acc[i] = chunk_dot(w[i], xp, acc[i]);
   }
   const float r = wave_reduce4(acc[0], acc[1], acc[2], acc[3]);
   const int slot = reduce4_slot(lane);
   if (slot >= 0 && row0 + slot < n) y[row0 + slot] = r * (scale[row0 + slot] * kCodeUnitInv);
+}
+
+template <int SW, int G, int R>
+void launch_gemv_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                     hipStream_t stream) {
+  const int64_t rows_per_block = static_cast<int64_t>(G) * R;
+  const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
+  hipLaunchKernelGGL((ternary_gemv_kernel<SW, G, R>), grid, dim3(SW * G * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
 }
 
 // Small M: lane l handles words l, l+64, ... of each row (16 codes each) so
@@ -107,10 +252,26 @@ void launch_small(const uint32_t* packed, const float* scale, int64_t n, int64_t
 
 hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
                                const uint16_t* x, float* y, hipStream_t stream) {
-  const int64_t rows_per_block = kGemvWaves * kRowsPerWave;
-  const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL(ternary_gemv_kernel, grid, dim3(kGemvWaves * kWave), 0, stream,
-                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
+  // One K-slice is 64 lanes x 64 codes = 4,096 columns.
+  const int64_t slices = (words_per_row(k) / 4 + kWave - 1) / kWave;
+  if (k % 8 != 0 || (reinterpret_cast<uintptr_t>(x) & 15u) != 0 || slices > 4) {
+    const dim3 grid(static_cast<unsigned>((n + 15) / 16));
+    hipLaunchKernelGGL(ternary_gemv_generic_kernel, grid, dim3(4 * kWave), 0, stream,
+                       reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
+    return hipGetLastError();
+  }
+  // Launch shapes measured on MI355X (rocprof, rotating weight pools): about
+  // 3-4 waves of few rows per SIMD, so that several waves decode at once.
+  switch (slices) {
+    case 1:
+      if (n >= 8192) launch_gemv_cfg<1, 4, 4>(packed, scale, n, k, x, y, stream);
+      else if (n >= 2048) launch_gemv_cfg<1, 8, 1>(packed, scale, n, k, x, y, stream);
+      else launch_gemv_cfg<1, 2, 1>(packed, scale, n, k, x, y, stream);
+      break;
+    case 2: launch_gemv_cfg<2, 4, 2>(packed, scale, n, k, x, y, stream); break;
+    case 3: launch_gemv_cfg<3, 4, 2>(packed, scale, n, k, x, y, stream); break;
+    default: launch_gemv_cfg<4, 4, 1>(packed, scale, n, k, x, y, stream); break;
+  }
   return hipGetLastError();
 }
 

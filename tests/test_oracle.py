@@ -51,20 +51,31 @@ def test_golden_words(case):
 
 
 def test_fp16_decode_property():
-    """rotr(word, 2t) & 0x84008400, read as two fp16 values, equals
-    (c[2t], c[2t+1]) * 2**-14: bit 10/26 set gives the smallest normal fp16
-    exponent, bit 15/31 is the fp16 sign."""
+    """(word << 2t) & 0xC000C000, read as two fp16 values, equals
+    (c[2t], c[2t+1]) * 2: bit 14/30 is the top fp16 exponent bit (2.0),
+    bit 15/31 is the fp16 sign."""
     codes = synth.ternary_codes(11, 64, 256)
     packed, _, _ = oracle.pack(codes)
     words = packed.reshape(-1).astype(np.uint64)
     c = codes.reshape(-1, 16).astype(np.float64)
     for t in range(8):
-        r = 2 * t
-        rot = ((words >> np.uint64(r)) | (words << np.uint64(32 - r))) & np.uint64(0xFFFFFFFF) if r else words
-        m = (rot & np.uint64(0x84008400)).astype(np.uint32)
-        halves = m.view(np.float16).reshape(-1, 2).astype(np.float64) * 2.0**14
+        shifted = (words << np.uint64(2 * t)) & np.uint64(0xFFFFFFFF)
+        m = (shifted & np.uint64(0xC000C000)).astype(np.uint32)
+        halves = m.view(np.float16).reshape(-1, 2).astype(np.float64) / 2.0
         assert np.array_equal(halves[:, 0], c[:, 2 * t])
         assert np.array_equal(halves[:, 1], c[:, 2 * t + 1])
+
+
+def test_fields_are_twos_complement():
+    """Each 2-bit field (sign, nonzero) read as a two's-complement integer is the code."""
+    codes = synth.ternary_codes(12, 8, 64)
+    packed, _, _ = oracle.pack(codes)
+    for j in range(16):
+        nz, sg = oracle.bit_positions(j)
+        assert sg == nz + 1
+        field = (packed[:, 0::1] >> np.uint32(nz)) & np.uint32(3)
+        val = np.where(field >= 2, field.astype(np.int64) - 4, field.astype(np.int64))
+        assert np.array_equal(val, codes.reshape(8, 4, 16)[:, :, j])
 
 
 @pytest.mark.slow
