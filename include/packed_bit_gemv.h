@@ -5,13 +5,13 @@
  *
  * What is computed (Neutrino-1 8B model page, English text on bittide):
  *   - every transformer linear is stored as ternary codes c in {-1, 0, +1}
- *     with a scale and a row sum per row, and is decoded inside the matrix
- *     kernels, never stored as fp16/fp32 weights (introduction; "Where the
+ *     with a scale and a row sum per row; the kernels expand the codes while
+ *     multiplying and never hold the weights as fp16/fp32 arrays (introduction; "Where the
  *     bytes live"; "Inside the coded lane");
- *   - the untied output head is an int8 tensor with one scale per row
+ *   - the untied output head is an int8 tensor with a per-row scale
  *     ("Where the bytes live");
- *   - a speculative verify pass scores a drafted run of tokens in one forward
- *     pass ("speculative" section), i.e. the same products for M <= 8 rows.
+ *   - speculative verification checks a whole drafted run of tokens with one
+ *     forward pass ("speculative" section), i.e. the same products for M <= 8 rows.
  *
  * Packed layout (this library's own; the page calls its format proprietary):
  *   - 2 bits per code, 16 codes per little-endian uint32 word;
@@ -96,8 +96,8 @@ int pack_ternary(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, in
 
 /*
  * ternary_gemv - y[r] = scale[r] * sum_j c[r][j] * x[j], one activation row.
- * Source: Neutrino-1 8B model page, introduction (codes decoded inside the
- * matrix kernels; decode bound by bytes moved per token) and "Where the bytes
+ * Source: Neutrino-1 8B model page, introduction (the kernels expand the
+ * codes; decode speed is set by the weight bytes read per token) and "Where the bytes
  * live" (per-row scale).
  *
  *   packed  [n][pbg_words_per_row(k)] uint32, 16-byte aligned
@@ -125,7 +125,7 @@ int ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, in
  * int8_head_gemv - Y[i][v] = scale[v] * sum_j w[v][j] * X[i][j] for the int8
  * output head, 1 <= m <= 8 activation rows.
  * Source: Neutrino-1 8B model page, "Where the bytes live" (untied int8
- * output head of 151,936 x 4,096 with one scale per row).
+ * output head of 151,936 x 4,096, a scale per row).
  *
  *   w       [n][k] int8, row-major, 16-byte aligned
  *   scale   [n] fp32, 4-byte aligned

@@ -9,13 +9,13 @@ generator with the HIP library, and it imports nothing from it.
 What it computes (Neutrino-1 8B model page, English text on bittide):
 
 * Every transformer linear is stored as ternary codes c in {-1, 0, +1} with a
-  scale and a row sum per row, and the codes are decoded inside the matrix
-  kernels (introduction; "Where the bytes live"; "Inside the coded lane").
+  scale and a row sum per row, and the kernels expand the codes themselves
+  while multiplying (introduction; "Where the bytes live"; "Inside the coded lane").
   The page calls the encoding proprietary and never specifies it, so the bit
   layout below is this project's own (2 bits per code, 16 codes per uint32).
   Its definition is stated here in words, once, and nowhere else in Python.
 * A linear applied to one activation row x is y_r = s_r * sum_j c_rj * x_j.
-* The untied output head is an int8 tensor with one scale per row
+* The untied output head is an int8 tensor with a per-row scale
   ("Where the bytes live"): y_v = s_v * sum_j w_vj * x_j.
 * The speculative verify pass scores a whole drafted run in one forward pass
   ("speculative" section), i.e. the same products for M activation rows.
@@ -175,7 +175,7 @@ def ternary_gemv(packed: np.ndarray, scale: np.ndarray, k: int, x: np.ndarray) -
 
 
 def int8_head_gemv(w: np.ndarray, scale: np.ndarray, x: np.ndarray, row_block: int = 8192) -> np.ndarray:
-    """Y[m, v] = s_v * sum_j w_vj * X[m, j] in fp64 (int8 head, one scale per row)."""
+    """Y[m, v] = s_v * sum_j w_vj * X[m, j] in fp64 (int8 head with per-row scales)."""
     w = np.asarray(w)
     if w.ndim != 2 or w.dtype != np.int8:
         raise ValueError("head weights must be a 2-D int8 array")

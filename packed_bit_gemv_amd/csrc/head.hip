@@ -1,5 +1,5 @@
 // int8_head_gemv: Y[i][v] = s_v * sum_j w_vj * X[i][j] for the untied int8
-// output head with one scale per row (Neutrino-1 8B model page, "Where the
+// output head with a per-row scale (Neutrino-1 8B model page, "Where the
 // bytes live"), for 1..8 activation rows.
 //
 // Each lane streams 16-byte chunks (16 weights) of 4 rows. A weight byte b is

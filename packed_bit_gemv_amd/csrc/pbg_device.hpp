@@ -36,6 +36,14 @@ __device__ __forceinline__ float word_dot(uint32_t w, const uint32_t* xp, float 
   return acc;
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed once, not kept in the caches).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ uint32_t as_u32(float v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ float as_f32(uint32_t v) { return __builtin_bit_cast(float, v); }
 

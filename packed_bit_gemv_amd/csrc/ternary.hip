@@ -1,8 +1,8 @@
 // ternary_gemv (M = 1) and ternary_gemm_small (M <= 8) for gfx950.
 //
 // y_r = s_r * sum_j c_rj * x_j with the codes decoded in registers from the
-// packed words (Neutrino-1 8B model page: codes decoded inside the matrix
-// kernels, introduction; per-row scale, "Where the bytes live"; a drafted run
+// packed words (Neutrino-1 8B model page: the kernels expand the codes
+// themselves, introduction; per-row scale, "Where the bytes live"; a drafted run
 // scored in one forward pass, "speculative").
 //
 // Work split (M = 1): a wave owns R consecutive rows and one 4,096-column
@@ -57,7 +57,7 @@ __device__ __forceinline__ float chunk_dot(const uint4& w, const uint32_t* xp, f
 //     fp16 pairs per lane, and the rows are decoded as they arrive.
 //  4. Rows are reduced four at a time across the wave; with SW > 1 the
 //     per-slice sums meet in LDS and are added in slice order.
-template <int SW, int G, int R>
+template <int SW, int G, int R, bool NT = false>
 __global__ __launch_bounds__(SW* G* kWave) void ternary_gemv_kernel(const uint4* __restrict__ packed,
                                                                      const float* __restrict__ scale, int64_t n,
                                                                      int64_t k, int64_t chunks,
@@ -93,7 +93,10 @@ __global__ __launch_bounds__(SW* G* kWave) void ternary_gemv_kernel(const uint4*
   const int64_t cc = c < chunks ? c : chunks - 1;
   uint4 w[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) w[i] = packed[(row0 + i < n ? row0 + i : n - 1) * chunks + cc];
+  for (int i = 0; i < R; ++i) {
+    const uint4* src = packed + (row0 + i < n ? row0 + i : n - 1) * chunks + cc;
+    w[i] = NT ? load_nt(src) : *src;
+  }
   const int slot = reduce4_slot(lane);
   float sc[kRed];
 #pragma unroll
@@ -188,12 +191,12 @@ __global__ __launch_bounds__(4 * kWave) void ternary_gemv_generic_kernel(const u
   if (slot >= 0 && row0 + slot < n) y[row0 + slot] = r * (scale[row0 + slot] * kCodeUnitInv);
 }
 
-template <int SW, int G, int R>
+template <int SW, int G, int R, bool NT = false>
 void launch_gemv_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
                      hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(G) * R;
   const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL((ternary_gemv_kernel<SW, G, R>), grid, dim3(SW * G * kWave), 0, stream,
+  hipLaunchKernelGGL((ternary_gemv_kernel<SW, G, R, NT>), grid, dim3(SW * G * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
 }
 
@@ -260,17 +263,18 @@ hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64
                        reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
     return hipGetLastError();
   }
-  // Launch shapes measured on MI355X (rocprof, rotating weight pools): about
-  // 3-4 waves of few rows per SIMD, so that several waves decode at once.
+  // Launch shapes measured on MI355X (rotating weight pools): about 3-4 waves
+  // of few rows per SIMD, so that several waves decode at once; weight loads
+  // are non-temporal (each byte is read once per call).
   switch (slices) {
     case 1:
-      if (n >= 8192) launch_gemv_cfg<1, 4, 4>(packed, scale, n, k, x, y, stream);
-      else if (n >= 2048) launch_gemv_cfg<1, 8, 1>(packed, scale, n, k, x, y, stream);
-      else launch_gemv_cfg<1, 2, 1>(packed, scale, n, k, x, y, stream);
+      if (n >= 8192) launch_gemv_cfg<1, 8, 3, true>(packed, scale, n, k, x, y, stream);
+      else if (n >= 2048) launch_gemv_cfg<1, 8, 1, true>(packed, scale, n, k, x, y, stream);
+      else launch_gemv_cfg<1, 2, 1, true>(packed, scale, n, k, x, y, stream);
       break;
-    case 2: launch_gemv_cfg<2, 4, 2>(packed, scale, n, k, x, y, stream); break;
-    case 3: launch_gemv_cfg<3, 4, 2>(packed, scale, n, k, x, y, stream); break;
-    default: launch_gemv_cfg<4, 4, 1>(packed, scale, n, k, x, y, stream); break;
+    case 2: launch_gemv_cfg<2, 4, 2, true>(packed, scale, n, k, x, y, stream); break;
+    case 3: launch_gemv_cfg<3, 4, 2, true>(packed, scale, n, k, x, y, stream); break;
+    default: launch_gemv_cfg<4, 4, 1, true>(packed, scale, n, k, x, y, stream); break;
   }
   return hipGetLastError();
 }

@@ -3,7 +3,7 @@
 This module only draws inputs: ternary codes, per-row scales, fp16 activation
 rows and int8 head weights, with the shapes and value statistics the Neutrino-1
 8B model page gives (geometry table; "Inside the coded lane" for the code
-distribution; "Where the bytes live" for the int8 head with one scale per row).
+distribution; "Where the bytes live" for the int8 head and its per-row scales).
 It holds none of the method's arithmetic: no packing, no decoding, no dot
 products. Both the CPU oracle side and the GPU side start from what it returns.
 
