@@ -242,6 +242,114 @@ __global__ __launch_bounds__(kGemvWaves* kWave) void ternary_gemm_small_kernel(c
   }
 }
 
+// Small M on the matrix cores (2 <= M <= 8, k % 8 == 0, x 16-byte aligned).
+// v_mfma_f32_16x16x32_f16 multiplies a 16-row tile of decoded codes (A,
+// 16 x 32) by up to 16 activation columns (B, 32 x 16; columns j >= M are
+// zero), so the cost per code does not grow with M. A lane with row i = lane
+// % 16 and K-group g = lane / 16 loads 16 bytes (64 codes) of its row per
+// 256-column unit u: codes 256u + 64g .. +63. MFMA step v (0..7) of the unit
+// takes codes 256u + 64g + 8v .. +7 of that lane (word v/2, half v%2, decoded
+// as 4 operand pairs), and the B lane (g, j) holds x_j at the same 8 columns,
+// so A and B agree on every column whatever order the unit uses inside a
+// K-group. The accumulator lane (g, j) holds rows 4g..4g+3 of column j.
+// A workgroup holds SK waves that split the units of T tiles; their partial
+// tiles meet in LDS and are added in wave order.
+template <int SK, int T, int UPW>
+__global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint4* __restrict__ packed,
+                                                                       const float* __restrict__ scale,
+                                                                       int64_t n, int64_t k, int64_t chunks,
+                                                                       const uint16_t* __restrict__ x, int m,
+                                                                       float* __restrict__ y) {
+  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+  typedef float float4_t __attribute__((ext_vector_type(4)));
+  constexpr int kRows = 16 * T;
+  __shared__ float part[SK][kRows][8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int64_t groups = k / 8;  // 8-column activation groups
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+
+  // scale of the output this thread writes at the end (row out_row, column out_col)
+  const int out_row = threadIdx.x >> 3, out_col = threadIdx.x & 7;
+  const int64_t srow = row_base + out_row;
+  const int64_t srow_c = row_base + (out_row < kRows ? out_row : kRows - 1);  // unconditional load
+  const float sc = scale[srow_c < n ? srow_c : n - 1];
+
+  // Loads of one unit: the B operands x_j of this lane's columns (zero for
+  // j >= m or past k) and one 16-byte chunk of A per tile.
+  auto load_unit = [&](int q, uint4 (&xb)[8], uint4 (&wv)[T]) {
+    const int64_t u = s + static_cast<int64_t>(SK) * q;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int64_t gi = 32 * u + 8 * lg + v;  // 8-column group within a row of x
+      const bool ok = li < m && gi < groups;
+      xb[v] = xg[ok ? static_cast<int64_t>(li) * groups + gi : 0];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t r = row_base + 16 * t + li;
+      const int64_t c = 4 * u + lg;
+      wv[t] = load_nt(packed + (r < n ? r : n - 1) * chunks + (c < chunks ? c : chunks - 1));
+    }
+  };
+
+  float4_t d[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xb[2][8], wv[2][T];
+  load_unit(0, xb[0], wv[0]);
+#pragma unroll
+  for (int q = 0; q < UPW; ++q) {
+    // the next unit's loads go out before this unit is decoded
+    if (q + 1 < UPW) load_unit(q + 1, xb[(q + 1) & 1], wv[(q + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t u = s + static_cast<int64_t>(SK) * q;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      uint4 bx = xb[q & 1][v];
+      const int64_t gi = 32 * u + 8 * lg + v;
+      const uint32_t keep = (li < m && gi < groups) ? 0xFFFFFFFFu : 0u;
+      bx.x &= keep;
+      bx.y &= keep;
+      bx.z &= keep;
+      bx.w &= keep;
+      const half8_t b = __builtin_bit_cast(half8_t, bx);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
+        const int h = v & 1;
+        const uint4 ap = make_uint4(code_pair(wd, 4 * h + 0), code_pair(wd, 4 * h + 1), code_pair(wd, 4 * h + 2),
+                                    code_pair(wd, 4 * h + 3));
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
+      }
+    }
+  }
+  // partial tiles to LDS: lane (g, j) holds rows 4g..4g+3 of column j
+  if (li < 8) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[s][16 * t + 4 * lg + r][li] = d[t][r];
+  }
+  __syncthreads();
+  if (out_row < kRows && out_col < m && srow < n) {
+    float sum = part[0][out_row][out_col];
+#pragma unroll
+    for (int w = 1; w < SK; ++w) sum += part[w][out_row][out_col];
+    y[static_cast<int64_t>(out_col) * n + srow] = sum * (sc * kCodeUnitInv);
+  }
+}
+
+template <int SK, int T, int UPW>
+void launch_mfma_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
+                     float* y, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
+  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW>), grid, dim3(SK * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y);
+}
+
 template <int M>
 void launch_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
                   hipStream_t stream) {
@@ -281,8 +389,21 @@ hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64
 
 hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
                                      const uint16_t* x, int m, float* y, hipStream_t stream) {
+  if (m == 1) return launch_ternary_gemv(packed, scale, n, k, x, y, stream);
+  const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
+  if (k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && units <= 3 * 16) {
+    // 16 waves split the units; tiles per workgroup keep 2-3 waves per SIMD.
+    if (units <= 16) {
+      if (n >= 8192) launch_mfma_cfg<16, 4, 1>(packed, scale, n, k, x, m, y, stream);
+      else launch_mfma_cfg<16, 1, 1>(packed, scale, n, k, x, m, y, stream);
+    } else if (units <= 32) {
+      launch_mfma_cfg<16, 2, 2>(packed, scale, n, k, x, m, y, stream);
+    } else {
+      launch_mfma_cfg<16, 2, 3>(packed, scale, n, k, x, m, y, stream);
+    }
+    return hipGetLastError();
+  }
   switch (m) {
-    case 1: launch_small<1>(packed, scale, n, k, x, y, stream); break;
     case 2: launch_small<2>(packed, scale, n, k, x, y, stream); break;
     case 3: launch_small<3>(packed, scale, n, k, x, y, stream); break;
     case 4: launch_small<4>(packed, scale, n, k, x, y, stream); break;
