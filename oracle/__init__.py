@@ -18,7 +18,12 @@ What it computes (Neutrino-1 8B model page, English text on bittide):
 * The untied output head is an int8 tensor with a per-row scale
   ("Where the bytes live"): y_v = s_v * sum_j w_vj * x_j.
 * The speculative verify pass scores a whole drafted run in one forward pass
-  ("speculative" section), i.e. the same products for M activation rows.
+  ("speculative" section), i.e. the same products for M activation rows, and a
+  drafted token is kept only when it equals the 8B's own argmax: the greedy
+  token of each row is the index of its largest head logit (lowest index
+  among equal maxima).
+* The int8 input embedding has a per-row scale and is read one row per token
+  ("Where the bytes live"): the embedding of token t is s_t * w_t.
 
 Bit layout of one 32-bit word (little-endian uint32) holding 16 codes:
   code j (0..15) belongs to pair t = j // 2 and half h = j % 2;
@@ -190,3 +195,31 @@ def int8_head_gemv(w: np.ndarray, scale: np.ndarray, x: np.ndarray, row_block: i
         sums = xs @ w[r0:r1].astype(np.float64).T
         y[:, r0:r1] = sums * scale[r0:r1].astype(np.float64)[None, :]
     return y
+
+
+def int8_head_argmax(w: np.ndarray, scale: np.ndarray, x: np.ndarray):
+    """Greedy token of each activation row: (argmax_v y[m, v] with the lowest
+    index among equal maxima, the fp64 logits y [m, n])."""
+    y = int8_head_gemv(w, scale, x)
+    return np.argmax(y, axis=1).astype(np.int64), y
+
+
+def embedding_gather(table: np.ndarray, scale: np.ndarray, tokens: np.ndarray) -> np.ndarray:
+    """Rows s_t * w_t of an int8 table with per-row scales, for token ids t.
+
+    The product of an fp32 scale and an int8 value is exact in fp64; it is
+    rounded once to fp32. Token ids outside [0, n) give a row of NaN.
+    """
+    table = np.asarray(table)
+    if table.ndim != 2 or table.dtype != np.int8:
+        raise ValueError("table must be a 2-D int8 array")
+    n, k = table.shape
+    scale = np.asarray(scale)
+    if scale.dtype != np.float32 or scale.shape != (n,):
+        raise ValueError("scale must be fp32 [n]")
+    tokens = np.asarray(tokens).astype(np.int64).reshape(-1)
+    out = np.full((tokens.size, k), np.nan, dtype=np.float32)
+    for i, t in enumerate(tokens):
+        if 0 <= t < n:
+            out[i] = (np.float64(scale[t]) * table[t].astype(np.float64)).astype(np.float32)
+    return out

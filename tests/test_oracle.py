@@ -260,3 +260,51 @@ def test_geometry_matches_printed_parameter_count():
     packed_layer = sum(synth.words_bytes(n, k) for n, k in synth.SHAPES.values())
     assert packed_layer == 48234496
     assert synth.HEAD_SHAPE == (g["vocab"], g["hidden"])
+
+
+# --------------------------------------------------------------------------
+# Greedy argmax and embedding rows
+# --------------------------------------------------------------------------
+def test_argmax_ties_lowest_index():
+    """Equal maxima resolve to the lowest row index."""
+    k = 64
+    w = np.zeros((10, k), dtype=np.int8)
+    w[3, 0] = 5
+    w[7, 0] = 5  # same logit as row 3
+    w[9, 0] = 4
+    s = np.ones(10, dtype=np.float32)
+    x = np.zeros((2, k), dtype=np.float16)
+    x[0, 0] = 1.0
+    x[1, 0] = -1.0  # all logits <= 0: rows with 0 tie, lowest is row 0
+    tok, y = oracle.int8_head_argmax(w, s, x)
+    assert tok.tolist() == [3, 0]
+    assert y[0, 3] == y[0, 7] == 5.0
+
+
+def test_argmax_matches_scan():
+    """Against a plain Python scan over exact integer logits."""
+    n, k = 300, 128
+    w = synth.int8_full_range(81, n, k)
+    x = synth.probe_activations(82, 3, k)
+    s = synth.pow2_scales(83, n)
+    tok, _ = oracle.int8_head_argmax(w, s, x)
+    for m in range(3):
+        vals = [float(s[v]) * sum(int(a) * int(b) for a, b in zip(w[v], x[m].astype(np.int64))) for v in range(n)]
+        best = 0
+        for v in range(1, n):
+            if vals[v] > vals[best]:
+                best = v
+        assert tok[m] == best
+
+
+def test_embedding_rows_exact():
+    """s_t * w_t rounded once to fp32, checked against Fraction arithmetic; out-of-range ids give NaN rows."""
+    n, k = 50, 33
+    table = synth.int8_full_range(84, n, k)
+    s = synth.row_scales(85, n)
+    tokens = np.array([0, 49, 7, 7, -1, 50])
+    out = oracle.embedding_gather(table, s, tokens)
+    for i, t in enumerate(tokens[:4]):
+        for j in range(k):
+            assert out[i, j] == np.float32(float(Fraction(float(s[t])) * int(table[t, j])))
+    assert np.all(np.isnan(out[4:]))
