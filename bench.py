@@ -316,6 +316,54 @@ def main():
             extra[f"layer_m{m}_GBs"] = round(lb / (ms * 1e-3) / 1e9, 1)
             del graphs
 
+        # greedy token through the head (logits never written)
+        keys = torch.empty(8, dtype=torch.int64, device=device)
+        tok = torch.empty(8, dtype=torch.int32, device=device)
+        lgt = torch.empty(8, dtype=torch.float32, device=device)
+        for m in (1, 7):
+            g = capture(torch, lambda m=m: pbg.int8_head_argmax(hw, hs, xs[hk][:m], keys[:m], tok[:m], lgt[:m]))
+            ms = time_graphs(torch, [g], 10, 2)
+            extra[f"head_argmax_m{m}_us"] = round(ms * 1e3, 2)
+            extra[f"head_argmax_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
+            del g
+
+        # shared-input fusion: q|k|v and gate|up as one packed matrix each
+        # (row concatenation of packs with the same K is itself a pack)
+        fused = []
+        for l in range(L):
+            lay = model.layers[l]
+            qkv = (torch.cat([lay[p][0] for p in ("q", "k", "v")]), torch.cat([lay[p][1] for p in ("q", "k", "v")]))
+            gu = (torch.cat([lay[p][0] for p in ("gate", "up")]), torch.cat([lay[p][1] for p in ("gate", "up")]))
+            fused.append((qkv, gu))
+        y_qkv = torch.empty(fused[0][0][0].shape[0], dtype=torch.float32, device=device)
+        y_gu = torch.empty(fused[0][1][0].shape[0], dtype=torch.float32, device=device)
+
+        def fused_ffn(l):
+            (gp, gs) = fused[l][1]
+            pbg.ternary_gemv(gp, gs, synth.HIDDEN, xs[synth.HIDDEN][0], y_gu)
+            linear(l, "down")
+
+        def fused_layer(l):
+            (qp, qs) = fused[l][0]
+            pbg.ternary_gemv(qp, qs, synth.HIDDEN, xs[synth.HIDDEN][0], y_qkv)
+            linear(l, "o")
+            fused_ffn(l)
+
+        ffn_bytes = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)
+        graphs = [capture(torch, lambda l=l: fused_ffn(l)) for l in range(L)]
+        ms = time_graphs(torch, graphs, K, W)
+        extra["ffn_fused_m1_us"] = round(ms * 1e3, 3)
+        extra["ffn_fused_m1_GBs"] = round(ffn_bytes / (ms * 1e-3) / 1e9, 1)
+        g = capture(torch, lambda: [fused_ffn(l) for l in range(L)])
+        ms = time_graphs(torch, [g], 5, 1) / L
+        extra["ffn_fused_m1_us_36_per_graph"] = round(ms * 1e3, 3)
+        extra["ffn_fused_m1_GBs_36_per_graph"] = round(ffn_bytes / (ms * 1e-3) / 1e9, 1)
+        g = capture(torch, lambda: [fused_layer(l) for l in range(L)])
+        ms = time_graphs(torch, [g], 5, 1) / L
+        extra["layer_fused_m1_us"] = round(ms * 1e3, 3)
+        extra["layer_fused_m1_GBs"] = round(layer_bytes / (ms * 1e-3) / 1e9, 1)
+        del graphs, g, fused
+
         # streaming-read ceiling at the gate byte count: torch copy over a pool
         nbytes = synth.words_bytes(*synth.SHAPES["gate"])
         pool = [torch.empty(nbytes // 4, dtype=torch.int32, device=device) for _ in range(48)]

@@ -135,6 +135,39 @@ int ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, in
 int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                    float* y, hipStream_t stream);
 
+/*
+ * int8_head_argmax - greedy token of each activation row through the int8
+ * head without writing the logits: token[i] = argmax_v Y[i][v] with Y as in
+ * int8_head_gemv, the lowest v among equal maxima; logit[i] = Y[i][token[i]].
+ * Source: Neutrino-1 8B model page, "speculative" section (a drafted token
+ * is accepted only when it equals the 8B's own argmax, so decoding stays the
+ * plain greedy stream) and "Where the bytes live" (int8 head).
+ *
+ *   w, scale, x, m  as int8_head_gemv (1 <= m <= 8); logits must be finite
+ *   keys    [m] uint64 device workspace, 8-byte aligned (cleared by the call)
+ *   token   [m] int32 out, 4-byte aligned
+ *   logit   [m] fp32 out, 4-byte aligned, or NULL
+ * The result does not depend on the order in which workgroups finish.
+ */
+int int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+                     uint64_t* keys, int32_t* token, float* logit, hipStream_t stream);
+
+/*
+ * int8_embedding_gather - out[i][j] = scale[t] * table[t][j] with t =
+ * tokens[i], formed exactly and rounded once to fp32.
+ * Source: Neutrino-1 8B model page, "Where the bytes live" (untied int8 input
+ * embedding, a scale per row, one row read per token).
+ *
+ *   table   [n][k] int8, row-major (any alignment)
+ *   scale   [n] fp32, 4-byte aligned
+ *   tokens  [m] int32 device, 4-byte aligned; ids outside [0, n) give a row
+ *           of NaN
+ *   out     [m][k] fp32 out, 4-byte aligned
+ *   1 <= m; m * ceil(k / 1024) <= 2^23
+ */
+int int8_embedding_gather(const int8_t* table, const float* scale, int64_t n, int64_t k, const int32_t* tokens,
+                          int64_t m, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

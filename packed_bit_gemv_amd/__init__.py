@@ -6,6 +6,8 @@ bits as the uint32 words of the C ABI).
 """
 from .binding import (  # noqa: F401
     PbgError,
+    int8_embedding_gather,
+    int8_head_argmax,
     int8_head_gemv,
     lib,
     pack_ternary,
@@ -16,6 +18,8 @@ from .binding import (  # noqa: F401
 
 __all__ = [
     "PbgError",
+    "int8_embedding_gather",
+    "int8_head_argmax",
     "int8_head_gemv",
     "lib",
     "pack_ternary",

@@ -30,6 +30,8 @@ _SIGNATURES = {
     "ternary_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "ternary_gemm_small": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "int8_head_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "int8_head_argmax": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _vp, _vp]),
+    "int8_embedding_gather": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
 }
 
 
@@ -186,3 +188,52 @@ def int8_head_gemv(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor,
     rc = lib().int8_head_gemv(w.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, y.data_ptr(), _stream(w))
     _check("int8_head_gemv", rc)
     return y
+
+
+def int8_head_argmax(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, keys: torch.Tensor | None = None,
+                     token: torch.Tensor | None = None, logit: torch.Tensor | None = None):
+    """Greedy token per activation row: (token int32 [m], logit fp32 [m]); keys is an int64 [m] workspace."""
+    _dev(w, "w", torch.int8)
+    _dev(scale, "scale", torch.float32)
+    _dev(x, "x", torch.float16)
+    if w.dim() != 2 or x.dim() != 2 or x.shape[1] != w.shape[1] or tuple(scale.shape) != (w.shape[0],):
+        raise ValueError("w [n, k], scale [n], x [m, k]")
+    n, k = w.shape
+    m = x.shape[0]
+    dev = w.device
+    if keys is None:
+        keys = torch.empty((m,), dtype=torch.int64, device=dev)
+    if token is None:
+        token = torch.empty((m,), dtype=torch.int32, device=dev)
+    if logit is None:
+        logit = torch.empty((m,), dtype=torch.float32, device=dev)
+    _dev(keys, "keys", torch.int64)
+    _dev(token, "token", torch.int32)
+    _dev(logit, "logit", torch.float32)
+    if keys.numel() != m or token.numel() != m or logit.numel() != m:
+        raise ValueError("keys, token and logit hold m entries")
+    rc = lib().int8_head_argmax(w.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, keys.data_ptr(),
+                                token.data_ptr(), logit.data_ptr(), _stream(w))
+    _check("int8_head_argmax", rc)
+    return token, logit
+
+
+def int8_embedding_gather(table: torch.Tensor, scale: torch.Tensor, tokens: torch.Tensor,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows scale[t] * table[t] (fp32 [m, k]) for int32 token ids; ids outside [0, n) give NaN rows."""
+    _dev(table, "table", torch.int8)
+    _dev(scale, "scale", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    if table.dim() != 2 or tokens.dim() != 1 or tuple(scale.shape) != (table.shape[0],):
+        raise ValueError("table [n, k], scale [n], tokens [m]")
+    n, k = table.shape
+    m = tokens.shape[0]
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.float32, device=table.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, k):
+        raise ValueError("out must be [m, k]")
+    rc = lib().int8_embedding_gather(table.data_ptr(), scale.data_ptr(), n, k, tokens.data_ptr(), m,
+                                     out.data_ptr(), _stream(table))
+    _check("int8_embedding_gather", rc)
+    return out

@@ -77,4 +77,25 @@ int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, co
   return finish(pbg::launch_int8_head(w, scale, n, k, x, static_cast<int>(m), y, stream));
 }
 
+int int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+                     uint64_t* keys, int32_t* token, float* logit, hipStream_t stream) {
+  if (!w || !scale || !x || !keys || !token) return PBG_ERR_NULL;
+  if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(w, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(keys, 8) || misaligned(token, 4) ||
+      misaligned(logit, 4))
+    return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_int8_head_argmax(w, scale, n, k, x, static_cast<int>(m),
+                                             reinterpret_cast<unsigned long long*>(keys), token, logit, stream));
+}
+
+int int8_embedding_gather(const int8_t* table, const float* scale, int64_t n, int64_t k, const int32_t* tokens,
+                          int64_t m, float* out, hipStream_t stream) {
+  if (!table || !scale || !tokens || !out) return PBG_ERR_NULL;
+  if (bad_nk(n, k) || m < 1 || m > PBG_MAX_N || pbg::embedding_blocks(m, k) > (1LL << 23)) return PBG_ERR_SHAPE;
+  if (misaligned(scale, 4) || misaligned(tokens, 4) || misaligned(out, 4)) return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_embedding_gather(table, scale, n, k, tokens, m, out, stream));
+}
+
 }  // extern "C"

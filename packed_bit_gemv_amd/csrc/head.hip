@@ -12,7 +12,7 @@
 namespace pbg {
 namespace {
 
-constexpr int kRowsPerWave = 4;
+constexpr int kHeadRows = 4;
 constexpr int kHeadWaves = 4;
 
 // Four int8 weights (one dword) -> two fp16 pairs (w0, w1), (w2, w3).
@@ -34,42 +34,49 @@ __device__ __forceinline__ uint4 load_w_chunk(const int8_t* __restrict__ row, in
   return make_uint4(q[0], q[1], q[2], q[3]);
 }
 
-template <int M>
+template <int M, bool AM>
 __global__ __launch_bounds__(kHeadWaves* kWave) void int8_head_kernel(const int8_t* __restrict__ w,
                                                                        const float* __restrict__ scale, int64_t n,
                                                                        int64_t k, const uint16_t* __restrict__ x,
-                                                                       float* __restrict__ y) {
+                                                                       float* __restrict__ y,
+                                                                       unsigned long long* __restrict__ keys) {
+  __shared__ unsigned long long wg_key[AM ? M : 1];
+  if constexpr (AM) {
+    if (threadIdx.x < M) wg_key[threadIdx.x] = 0ull;
+    __syncthreads();
+  }
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kHeadWaves + (threadIdx.x / kWave)) * kRowsPerWave;
-  if (row0 >= n) return;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kHeadWaves + (threadIdx.x / kWave)) * kHeadRows;
   const int64_t chunks = (k + 15) / 16;
   const bool vec = (k % 16 == 0);
-  float acc[kRowsPerWave][M];
+  float acc[kHeadRows][M];
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i)
+  for (int i = 0; i < kHeadRows; ++i)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[i][m] = 0.0f;
-  for (int64_t c = lane; c < chunks; c += kWave) {
-    uint32_t xp[M][8];
+  if (row0 < n) {  // wave-uniform
+    for (int64_t c = lane; c < chunks; c += kWave) {
+      uint32_t xp[M][8];
 #pragma unroll
-    for (int m = 0; m < M; ++m) load_x_pairs<8>(x + m * k, k, 16 * c, xp[m]);
-    uint4 wv[kRowsPerWave];
+      for (int m = 0; m < M; ++m) load_x_pairs<8>(x + m * k, k, 16 * c, xp[m]);
+      uint4 wv[kHeadRows];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i)
-      wv[i] = (row0 + i < n) ? load_w_chunk(w + (row0 + i) * k, k, 16 * c, vec) : make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < kHeadRows; ++i)
+        wv[i] = (row0 + i < n) ? load_w_chunk(w + (row0 + i) * k, k, 16 * c, vec) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      uint32_t hp[8];
-      int8x4_to_half2x2(wv[i].x, hp[0], hp[1]);
-      int8x4_to_half2x2(wv[i].y, hp[2], hp[3]);
-      int8x4_to_half2x2(wv[i].z, hp[4], hp[5]);
-      int8x4_to_half2x2(wv[i].w, hp[6], hp[7]);
+      for (int i = 0; i < kHeadRows; ++i) {
+        uint32_t hp[8];
+        int8x4_to_half2x2(wv[i].x, hp[0], hp[1]);
+        int8x4_to_half2x2(wv[i].y, hp[2], hp[3]);
+        int8x4_to_half2x2(wv[i].z, hp[4], hp[5]);
+        int8x4_to_half2x2(wv[i].w, hp[6], hp[7]);
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float a = acc[i][m];
+        for (int m = 0; m < M; ++m) {
+          float a = acc[i][m];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) a = dot2(hp[p], xp[m][p], a);
-        acc[i][m] = a;
+          for (int p = 0; p < 8; ++p) a = dot2(hp[p], xp[m][p], a);
+          acc[i][m] = a;
+        }
       }
     }
   }
@@ -77,16 +84,24 @@ __global__ __launch_bounds__(kHeadWaves* kWave) void int8_head_kernel(const int8
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const float r = wave_reduce4(acc[0][m], acc[1][m], acc[2][m], acc[3][m]);
-    if (slot >= 0 && row0 + slot < n) y[m * n + row0 + slot] = r * scale[row0 + slot];
+    if (slot >= 0 && row0 + slot < n) {
+      const float v = r * scale[row0 + slot];
+      if constexpr (AM) atomicMax(&wg_key[m], argmax_key(v, row0 + slot));
+      else y[m * n + row0 + slot] = v;
+    }
+  }
+  if constexpr (AM) {
+    __syncthreads();
+    if (threadIdx.x < M) atomicMax(&keys[threadIdx.x], wg_key[threadIdx.x]);
   }
 }
 
-template <int M>
+template <int M, bool AM>
 void launch_head_m(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
-                   hipStream_t stream) {
-  const int64_t rows_per_block = kHeadWaves * kRowsPerWave;
+                   unsigned long long* keys, hipStream_t stream) {
+  const int64_t rows_per_block = kHeadWaves * kHeadRows;
   const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL(int8_head_kernel<M>, grid, dim3(kHeadWaves * kWave), 0, stream, w, scale, n, k, x, y);
+  hipLaunchKernelGGL((int8_head_kernel<M, AM>), grid, dim3(kHeadWaves * kWave), 0, stream, w, scale, n, k, x, y, keys);
 }
 
 // Fast path (k % 16 == 0, w and x 16-byte aligned). A workgroup holds G row
@@ -97,11 +112,17 @@ void launch_head_m(const int8_t* w, const float* scale, int64_t n, int64_t k, co
 // conversion, and the row scales are prefetched. Partial sums are reduced
 // four at a time across the wave, then added over the SW slices in order in
 // LDS.
-template <int M, int SW, int G, int R>
+template <int M, int SW, int G, int R, bool AM>
 __global__ __launch_bounds__(SW* G* kWave) void int8_head_fast_kernel(const int8_t* __restrict__ w,
                                                                        const float* __restrict__ scale, int64_t n,
                                                                        int64_t k, const uint16_t* __restrict__ x,
-                                                                       float* __restrict__ y) {
+                                                                       float* __restrict__ y,
+                                                                       unsigned long long* __restrict__ keys) {
+  __shared__ unsigned long long wg_key[AM ? M : 1];
+  if constexpr (AM) {
+    if (threadIdx.x < M) wg_key[threadIdx.x] = 0ull;
+    __syncthreads();
+  }
   constexpr int kVals = R * M;  // partial sums per lane: (row i, activation row m) at i * M + m
   constexpr int kRed = (kVals + 3) / 4;
   const int lane = threadIdx.x & (kWave - 1);
@@ -181,7 +202,11 @@ __global__ __launch_bounds__(SW* G* kWave) void int8_head_fast_kernel(const int8
       for (int q = 0; q < kRed; ++q) {
         const int idx = 4 * q + slot;
         const int64_t r = row0 + idx / M;
-        if (idx < kVals && r < n) y[static_cast<int64_t>(idx % M) * n + r] = red[q] * sc[q];
+        if (idx < kVals && r < n) {
+          const float v = red[q] * sc[q];
+          if constexpr (AM) atomicMax(&wg_key[idx % M], argmax_key(v, r));
+          else y[static_cast<int64_t>(idx % M) * n + r] = v;
+        }
       }
     }
   } else {
@@ -200,53 +225,215 @@ __global__ __launch_bounds__(SW* G* kWave) void int8_head_fast_kernel(const int8
           float sum = part[g][0][idx];
 #pragma unroll
           for (int t = 1; t < SW; ++t) sum += part[g][t][idx];
-          y[static_cast<int64_t>(idx % M) * n + r] = sum * sc[q];
+          const float v = sum * sc[q];
+          if constexpr (AM) atomicMax(&wg_key[idx % M], argmax_key(v, r));
+          else y[static_cast<int64_t>(idx % M) * n + r] = v;
         }
       }
     }
   }
+  if constexpr (AM) {
+    __syncthreads();
+    if (threadIdx.x < M) atomicMax(&keys[threadIdx.x], wg_key[threadIdx.x]);
+  }
 }
 
-template <int M, int SW, int G, int R>
+template <int M, int SW, int G, int R, bool AM>
 void launch_head_fast(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
-                      hipStream_t stream) {
+                      unsigned long long* keys, hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(G) * R;
   const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL((int8_head_fast_kernel<M, SW, G, R>), grid, dim3(SW * G * kWave), 0, stream, w, scale, n, k, x,
-                     y);
+  hipLaunchKernelGGL((int8_head_fast_kernel<M, SW, G, R, AM>), grid, dim3(SW * G * kWave), 0, stream, w, scale, n, k,
+                     x, y, keys);
 }
 
-template <int M>
-void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
-                     hipStream_t stream) {
-  // The register-resident fast path wins at M = 1 (measured); with more rows
-  // its per-lane accumulators crowd out waves, and the wave-per-4-rows kernel
-  // is faster.
-  const bool fast = M == 1 && k % 16 == 0 && (reinterpret_cast<uintptr_t>(w) & 15u) == 0 &&
-                    (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
-  if (!fast) {
-    launch_head_m<M>(w, scale, n, k, x, y, stream);
-    return;
+// 2 <= M <= 8 on the matrix cores (k % 16 == 0, w and x 16-byte aligned).
+// v_mfma_f32_16x16x32_f16 takes a 16-row tile of weights converted to fp16
+// (A) and the M activation rows as B columns (zero past M). A lane with row
+// i = lane % 16 and K-group g = lane / 16 loads 16 weights per 64-column unit
+// u: columns 64u + 16g .. +15; MFMA step v (0, 1) uses columns 64u + 16g + 8v
+// .. +7, and the B lane (g, j) holds x_j at the same columns. SK waves split
+// the units of T tiles; the next unit's loads go out before the current one
+// is converted; partial tiles meet in LDS and are added in wave order.
+template <int SK, int T, int UPW, bool AM>
+__global__ __launch_bounds__(SK* kWave) void int8_head_mfma_kernel(const int8_t* __restrict__ w,
+                                                                    const float* __restrict__ scale, int64_t n,
+                                                                    int64_t k, const uint16_t* __restrict__ x, int m,
+                                                                    float* __restrict__ y,
+                                                                    unsigned long long* __restrict__ keys) {
+  __shared__ unsigned long long wg_key[AM ? 8 : 1];
+  if constexpr (AM) {
+    if (threadIdx.x < 8) wg_key[threadIdx.x] = 0ull;  // ordered before use by the barrier below
   }
-  constexpr int kR = M <= 2 ? 8 : 4;
-  launch_head_fast<M, 4, 2, kR>(w, scale, n, k, x, y, stream);
+  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+  typedef float float4_t __attribute__((ext_vector_type(4)));
+  constexpr int kRows = 16 * T;
+  __shared__ float part[SK][kRows][8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int64_t chunks = k / 16, groups = k / 8;
+  const uint4* wq = reinterpret_cast<const uint4*>(w);
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+
+  // Outputs (row, column) o = threadIdx.x + e * SK * 64 of the tile block,
+  // row o / 8 and column o % 8; their scales are fetched now.
+  constexpr int kOut = (kRows * 8 + SK * kWave - 1) / (SK * kWave);
+  float sc[kOut];
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    const int64_t r = row_base + (o < kRows * 8 ? o >> 3 : kRows - 1);
+    sc[e] = scale[r < n ? r : n - 1];
+  }
+
+  auto load_unit = [&](int q, uint4 (&xb)[2], uint4 (&wv)[T]) {
+    const int64_t u = s + static_cast<int64_t>(SK) * q;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int64_t gi = 8 * u + 2 * lg + v;
+      const bool ok = li < m && gi < groups;
+      xb[v] = xg[ok ? static_cast<int64_t>(li) * groups + gi : 0];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t r = row_base + 16 * t + li;
+      const int64_t c = 4 * u + lg;
+      wv[t] = load_nt(wq + (r < n ? r : n - 1) * chunks + (c < chunks ? c : chunks - 1));
+    }
+  };
+
+  float4_t d[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xb[2][2], wv[2][T];
+  load_unit(0, xb[0], wv[0]);
+#pragma unroll
+  for (int q = 0; q < UPW; ++q) {
+    if (q + 1 < UPW) load_unit(q + 1, xb[(q + 1) & 1], wv[(q + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t u = s + static_cast<int64_t>(SK) * q;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      uint4 bx = xb[q & 1][v];
+      const int64_t gi = 8 * u + 2 * lg + v;
+      const uint32_t keep = (li < m && gi < groups) ? 0xFFFFFFFFu : 0u;
+      bx.x &= keep;
+      bx.y &= keep;
+      bx.z &= keep;
+      bx.w &= keep;
+      const half8_t b = __builtin_bit_cast(half8_t, bx);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t w0 = v == 0 ? wv[q & 1][t].x : wv[q & 1][t].z;
+        const uint32_t w1 = v == 0 ? wv[q & 1][t].y : wv[q & 1][t].w;
+        uint4 ap;
+        int8x4_to_half2x2(w0, ap.x, ap.y);
+        int8x4_to_half2x2(w1, ap.z, ap.w);
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
+      }
+    }
+  }
+  if (li < 8) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[s][16 * t + 4 * lg + r][li] = d[t][r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    const int orow = o >> 3, ocol = o & 7;
+    const int64_t r = row_base + orow;
+    if (o < kRows * 8 && ocol < m && r < n) {
+      float sum = part[0][orow][ocol];
+#pragma unroll
+      for (int w2 = 1; w2 < SK; ++w2) sum += part[w2][orow][ocol];
+      const float v = sum * sc[e];
+      if constexpr (AM) atomicMax(&wg_key[ocol], argmax_key(v, r));
+      else y[static_cast<int64_t>(ocol) * n + r] = v;
+    }
+  }
+  if constexpr (AM) {
+    __syncthreads();
+    if (threadIdx.x < m) atomicMax(&keys[threadIdx.x], wg_key[threadIdx.x]);
+  }
+}
+
+template <int SK, int T, int UPW, bool AM>
+void launch_head_mfma(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m, float* y,
+                      unsigned long long* keys, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
+  hipLaunchKernelGGL((int8_head_mfma_kernel<SK, T, UPW, AM>), grid, dim3(SK * kWave), 0, stream, w, scale, n, k, x, m,
+                     y, keys);
+}
+
+template <int M, bool AM>
+void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                     unsigned long long* keys, hipStream_t stream) {
+  const bool aligned = k % 16 == 0 && (reinterpret_cast<uintptr_t>(w) & 15u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  const int64_t units = (k / 16 + 3) / 4;  // 64-column units
+  if (aligned && M == 1) {
+    launch_head_fast<1, 4, 2, 8, AM>(w, scale, n, k, x, y, keys, stream);
+  } else if (aligned && M >= 3 && units <= 8 * 16) {
+    // 8 waves split the units of 4 tiles (64 rows); at M = 2 the
+    // wave-per-4-rows kernel is faster (measured).
+    if (units <= 8) launch_head_mfma<8, 4, 1, AM>(w, scale, n, k, x, M, y, keys, stream);
+    else if (units <= 16) launch_head_mfma<8, 4, 2, AM>(w, scale, n, k, x, M, y, keys, stream);
+    else if (units <= 32) launch_head_mfma<8, 4, 4, AM>(w, scale, n, k, x, M, y, keys, stream);
+    else if (units <= 64) launch_head_mfma<8, 4, 8, AM>(w, scale, n, k, x, M, y, keys, stream);
+    else launch_head_mfma<8, 4, 16, AM>(w, scale, n, k, x, M, y, keys, stream);
+  } else {
+    launch_head_m<M, AM>(w, scale, n, k, x, y, keys, stream);
+  }
+}
+
+__global__ void argmax_init_kernel(unsigned long long* keys, int m) {
+  if (threadIdx.x < m) keys[threadIdx.x] = 0ull;
+}
+
+__global__ void argmax_finish_kernel(const unsigned long long* __restrict__ keys, int m, int32_t* __restrict__ token,
+                                     float* __restrict__ logit) {
+  if (threadIdx.x < m) {
+    const unsigned long long key = keys[threadIdx.x];
+    token[threadIdx.x] = argmax_key_row(key);
+    if (logit) logit[threadIdx.x] = argmax_key_logit(key);
+  }
+}
+
+template <bool AM>
+hipError_t dispatch_head(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m, float* y,
+                         unsigned long long* keys, hipStream_t stream) {
+  switch (m) {
+    case 1: launch_head_any<1, AM>(w, scale, n, k, x, y, keys, stream); break;
+    case 2: launch_head_any<2, AM>(w, scale, n, k, x, y, keys, stream); break;
+    case 3: launch_head_any<3, AM>(w, scale, n, k, x, y, keys, stream); break;
+    case 4: launch_head_any<4, AM>(w, scale, n, k, x, y, keys, stream); break;
+    case 5: launch_head_any<5, AM>(w, scale, n, k, x, y, keys, stream); break;
+    case 6: launch_head_any<6, AM>(w, scale, n, k, x, y, keys, stream); break;
+    case 7: launch_head_any<7, AM>(w, scale, n, k, x, y, keys, stream); break;
+    case 8: launch_head_any<8, AM>(w, scale, n, k, x, y, keys, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_int8_head(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
                             float* y, hipStream_t stream) {
-  switch (m) {
-    case 1: launch_head_any<1>(w, scale, n, k, x, y, stream); break;
-    case 2: launch_head_any<2>(w, scale, n, k, x, y, stream); break;
-    case 3: launch_head_any<3>(w, scale, n, k, x, y, stream); break;
-    case 4: launch_head_any<4>(w, scale, n, k, x, y, stream); break;
-    case 5: launch_head_any<5>(w, scale, n, k, x, y, stream); break;
-    case 6: launch_head_any<6>(w, scale, n, k, x, y, stream); break;
-    case 7: launch_head_any<7>(w, scale, n, k, x, y, stream); break;
-    case 8: launch_head_any<8>(w, scale, n, k, x, y, stream); break;
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch_head<false>(w, scale, n, k, x, m, y, nullptr, stream);
+}
+
+hipError_t launch_int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
+                                   unsigned long long* keys, int32_t* token, float* logit, hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_init_kernel, dim3(1), dim3(kWave), 0, stream, keys, m);
+  const hipError_t e = dispatch_head<true>(w, scale, n, k, x, m, nullptr, keys, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(1), dim3(kWave), 0, stream, keys, m, token, logit);
   return hipGetLastError();
 }
 

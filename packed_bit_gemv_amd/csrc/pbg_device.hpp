@@ -85,6 +85,25 @@ __device__ __forceinline__ int reduce4_slot(int lane) {
   return lane == 0 ? 0 : lane == 32 ? 1 : lane == 16 ? 2 : lane == 48 ? 3 : -1;
 }
 
+// Greedy-argmax key of a logit: the order-preserving image of the fp32 bits
+// in the high half and (2^32 - 1 - row) in the low half, so that the largest
+// key is the largest logit and, among equal logits, the lowest row. Logits
+// are finite.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int64_t row) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<unsigned long long>(ord) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(row));
+}
+
+__device__ __forceinline__ float argmax_key_logit(unsigned long long key) {
+  const uint32_t ord = static_cast<uint32_t>(key >> 32);
+  return __builtin_bit_cast(float, (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__device__ __forceinline__ int32_t argmax_key_row(unsigned long long key) {
+  return static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
 // Loads x[base .. base+2*NPAIR-1] as NPAIR fp16 pairs; columns >= k read 0.
 template <int NPAIR>
 __device__ __forceinline__ void load_x_pairs(const uint16_t* __restrict__ x, int64_t k, int64_t base,

@@ -18,6 +18,15 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
 hipError_t launch_int8_head(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
                             int m, float* y, hipStream_t stream);
 
+hipError_t launch_int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                                   int m, unsigned long long* keys, int32_t* token, float* logit, hipStream_t stream);
+
+hipError_t launch_embedding_gather(const int8_t* table, const float* scale, int64_t n, int64_t k,
+                                   const int32_t* tokens, int64_t m, float* out, hipStream_t stream);
+
+// Workgroups one embedding gather launches (the grid must stay below 2^31 / 256).
+int64_t embedding_blocks(int64_t m, int64_t k);
+
 inline int64_t words_per_row(int64_t k) { return k <= 0 ? 0 : 4 * ((k + 63) / 64); }
 
 }  // namespace pbg

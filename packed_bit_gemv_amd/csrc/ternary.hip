@@ -271,11 +271,16 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
   const int64_t groups = k / 8;  // 8-column activation groups
   const uint4* xg = reinterpret_cast<const uint4*>(x);
 
-  // scale of the output this thread writes at the end (row out_row, column out_col)
-  const int out_row = threadIdx.x >> 3, out_col = threadIdx.x & 7;
-  const int64_t srow = row_base + out_row;
-  const int64_t srow_c = row_base + (out_row < kRows ? out_row : kRows - 1);  // unconditional load
-  const float sc = scale[srow_c < n ? srow_c : n - 1];
+  // Outputs (row, column) o = threadIdx.x + e * SK * 64 of the tile block,
+  // row o / 8 and column o % 8; their scales are fetched now.
+  constexpr int kOut = (kRows * 8 + SK * kWave - 1) / (SK * kWave);
+  float sc[kOut];
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    const int64_t r = row_base + (o < kRows * 8 ? o >> 3 : kRows - 1);
+    sc[e] = scale[r < n ? r : n - 1];
+  }
 
   // Loads of one unit: the B operands x_j of this lane's columns (zero for
   // j >= m or past k) and one 16-byte chunk of A per tile.
@@ -334,11 +339,17 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
       for (int r = 0; r < 4; ++r) part[s][16 * t + 4 * lg + r][li] = d[t][r];
   }
   __syncthreads();
-  if (out_row < kRows && out_col < m && srow < n) {
-    float sum = part[0][out_row][out_col];
 #pragma unroll
-    for (int w = 1; w < SK; ++w) sum += part[w][out_row][out_col];
-    y[static_cast<int64_t>(out_col) * n + srow] = sum * (sc * kCodeUnitInv);
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    const int orow = o >> 3, ocol = o & 7;
+    const int64_t r = row_base + orow;
+    if (o < kRows * 8 && ocol < m && r < n) {
+      float sum = part[0][orow][ocol];
+#pragma unroll
+      for (int w = 1; w < SK; ++w) sum += part[w][orow][ocol];
+      y[static_cast<int64_t>(ocol) * n + r] = sum * (sc[e] * kCodeUnitInv);
+    }
   }
 }
 
@@ -391,15 +402,16 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
                                      const uint16_t* x, int m, float* y, hipStream_t stream) {
   if (m == 1) return launch_ternary_gemv(packed, scale, n, k, x, y, stream);
   const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
-  if (k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && units <= 3 * 16) {
-    // 16 waves split the units; tiles per workgroup keep 2-3 waves per SIMD.
+  if (k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && units <= 48) {
+    // Launch shapes from a sweep on MI355X at M = 4 and 8: more tiles per
+    // workgroup (each activation column reused by more rows) beat more waves.
     if (units <= 16) {
-      if (n >= 8192) launch_mfma_cfg<16, 4, 1>(packed, scale, n, k, x, m, y, stream);
-      else launch_mfma_cfg<16, 1, 1>(packed, scale, n, k, x, m, y, stream);
+      if (n >= 8192) launch_mfma_cfg<4, 4, 4>(packed, scale, n, k, x, m, y, stream);
+      else launch_mfma_cfg<4, 1, 4>(packed, scale, n, k, x, m, y, stream);
     } else if (units <= 32) {
-      launch_mfma_cfg<16, 2, 2>(packed, scale, n, k, x, m, y, stream);
+      launch_mfma_cfg<4, 1, 8>(packed, scale, n, k, x, m, y, stream);
     } else {
-      launch_mfma_cfg<16, 2, 3>(packed, scale, n, k, x, m, y, stream);
+      launch_mfma_cfg<4, 1, 12>(packed, scale, n, k, x, m, y, stream);
     }
     return hipGetLastError();
   }

@@ -34,6 +34,7 @@ no_gpu_only = pytest.mark.skipif("_gpu_visible()", reason="fake-pointer calls ar
 def test_exports_every_header_function():
     names = binding.header_functions()
     assert set(names) >= {"pack_ternary", "ternary_gemv", "ternary_gemm_small", "int8_head_gemv",
+                          "int8_head_argmax", "int8_embedding_gather",
                           "pbg_abi_version", "pbg_strerror", "pbg_words_per_row"}
     lib = binding.lib()
     for name in names:
@@ -59,6 +60,9 @@ def test_null_pointers():
     assert lib.ternary_gemm_small(GOOD, None, 4, 64, GOOD, 2, GOOD, None) == -1
     assert lib.int8_head_gemv(GOOD, GOOD, 4, 64, GOOD, 1, None, None) == -1
     assert lib.pack_ternary(GOOD, 4, 64, GOOD, GOOD, None, None, None) == -1
+    assert lib.int8_head_argmax(GOOD, GOOD, 4, 64, GOOD, 1, None, GOOD, None, None) == -1
+    assert lib.int8_head_argmax(GOOD, GOOD, 4, 64, GOOD, 1, GOOD, None, None, None) == -1
+    assert lib.int8_embedding_gather(GOOD, GOOD, 4, 64, None, 2, GOOD, None) == -1
 
 
 @no_gpu_only
@@ -68,6 +72,7 @@ def test_bad_shapes(n, k, m):
     lib = binding.lib()
     assert lib.ternary_gemm_small(GOOD, GOOD, n, k, GOOD, m, GOOD, None) == -2
     assert lib.int8_head_gemv(GOOD, GOOD, n, k, GOOD, m, GOOD, None) == -2
+    assert lib.int8_head_argmax(GOOD, GOOD, n, k, GOOD, m, GOOD, GOOD, None, None) == -2
     if m == 1:
         assert lib.ternary_gemv(GOOD, GOOD, n, k, GOOD, GOOD, None) == -2
         assert lib.pack_ternary(GOOD, n, k, GOOD, GOOD, GOOD, None, None) == -2
@@ -84,6 +89,18 @@ def test_misaligned():
     assert lib.ternary_gemm_small(GOOD + 8, GOOD, 4, 64, GOOD, 2, GOOD, None) == -3
     assert lib.pack_ternary(GOOD, 4, 64, GOOD + 4, GOOD, GOOD, None, None) == -3
     assert lib.pack_ternary(GOOD, 4, 64, GOOD, GOOD, GOOD + 4, None, None) == -3
+    assert lib.int8_head_argmax(GOOD, GOOD, 4, 64, GOOD, 1, GOOD + 4, GOOD, None, None) == -3
+    assert lib.int8_head_argmax(GOOD, GOOD, 4, 64, GOOD, 1, GOOD, GOOD + 2, None, None) == -3
+    assert lib.int8_embedding_gather(GOOD + 1, GOOD + 2, 4, 64, GOOD, 2, GOOD, None) == -3
+    assert lib.int8_embedding_gather(GOOD, GOOD, 4, 64, GOOD + 2, 2, GOOD, None) == -3
+
+
+@no_gpu_only
+def test_embedding_shapes():
+    lib = binding.lib()
+    assert lib.int8_embedding_gather(GOOD, GOOD, 4, 64, GOOD, 0, GOOD, None) == -2
+    assert lib.int8_embedding_gather(GOOD, GOOD, 0, 64, GOOD, 2, GOOD, None) == -2
+    assert lib.int8_embedding_gather(GOOD, GOOD, 4, 4096, GOOD, 2 ** 22, GOOD, None) == -2
 
 
 def test_binding_rejects_cpu_tensors():

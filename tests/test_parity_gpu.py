@@ -192,7 +192,8 @@ def test_gemv_full_size_sampled(pbg):
 # ternary_gemm_small (M <= 8)
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("n,k", [(5, 16), (17, 65), (40, 4096), (21, 8200), (64, 12288)])
+@pytest.mark.parametrize("n,k", [(5, 16), (17, 65), (40, 4096), (21, 8200), (64, 12288), (8200, 4096),
+                                 (1000, 12288)])
 def test_small_m_exact_probe(pbg, m, n, k):
     say(f"small-m exact m={m} n={n} k={k}")
     codes = synth.ternary_codes(8000 + n + k, n, k)
@@ -222,7 +223,7 @@ def test_small_m_config_shapes(pbg, m, proj):
 # int8_head_gemv
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("n,k", [(1, 16), (3, 5), (17, 100), (40, 4096), (33, 4112), (9, 12288)])
+@pytest.mark.parametrize("n,k", [(1, 16), (3, 5), (17, 100), (40, 4096), (33, 4112), (9, 12288), (1000, 4096)])
 def test_head_exact_probe(pbg, m, n, k):
     say(f"head exact m={m} n={n} k={k}")
     w = synth.int8_full_range(10000 + n + k, n, k)
@@ -325,3 +326,96 @@ def test_graph_replay_matches_eager(pbg):
         assert torch.equal(y1, ref[0]) and torch.equal(y4, ref[1]) and torch.equal(yh, ref[2]), rep
         pbg.ternary_gemv(p, s, k, x[1], torch.empty_like(y1))  # eager work between replays
         torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# Greedy argmax through the head, embedding rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("n,k", [(1, 16), (17, 100), (40, 4096), (33, 4112), (2000, 4096), (9, 12288)])
+def test_head_argmax_exact_probe(pbg, m, n, k):
+    """Integer activations, power-of-two scales, full-range int8: logits are
+    exact on both sides, so the token (lowest index on ties) and its logit
+    must equal the oracle's."""
+    say(f"argmax exact m={m} n={n} k={k}")
+    w = synth.int8_full_range(16000 + n + k, n, k)
+    w[n // 2] = w[0]  # a guaranteed tie in every row of X when row 0 wins
+    x = synth.probe_activations(17000 + m, m, k)
+    s = synth.pow2_scales(18000 + n, n)
+    s[n // 2] = s[0]
+    tok_ref, y_ref = oracle.int8_head_argmax(w, s, x)
+    tok, logit = pbg.int8_head_argmax(dev(w), dev(s), dev(x))
+    assert tok.cpu().numpy().tolist() == tok_ref.tolist()
+    assert np.array_equal(logit.cpu().numpy().astype(np.float64), y_ref[np.arange(m), tok_ref])
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 7, 8])
+def test_head_argmax_random(pbg, m):
+    n, k = 5003, 4096
+    say(f"argmax random m={m}")
+    w = synth.head_weights(19000, n, k)
+    x = synth.activations(19100 + m, m, k)
+    s = synth.row_scales(19200, n)
+    tok_ref, y_ref = oracle.int8_head_argmax(w, s, x)
+    bound = head_bound(w, s, x)
+    tok, logit = pbg.int8_head_argmax(dev(w), dev(s), dev(x))
+    tok = tok.cpu().numpy()
+    y_gpu = pbg.int8_head_gemv(dev(w), dev(s), dev(x)).cpu().numpy()
+    for i in range(m):
+        t = int(tok[i])
+        # a valid argmax of the exact logits within the error bounds
+        assert y_ref[i, t] >= np.max(y_ref[i] - bound[i]) - bound[i, t]
+        # the same logit and the lowest-index maximum of the kernel's own logits
+        assert logit.cpu().numpy()[i] == y_gpu[i, t]
+        assert t == int(np.argmax(y_gpu[i]))
+        gap = np.sort(y_ref[i])[-1] - np.sort(y_ref[i])[-2]
+        if gap > 2 * bound[i].max():
+            assert t == tok_ref[i]
+
+
+@pytest.mark.parametrize("m", [1, 7])
+def test_head_argmax_full_size(pbg, m):
+    n, k = synth.HEAD_SHAPE
+    say(f"argmax full head m={m}")
+    w = synth.head_weights_device(synth.SEED_HEAD, n, k, "cuda:0")
+    s = synth.row_scales_device(synth.SEED_HEAD, n, "cuda:0")
+    x = synth.activations(synth.x_seed(0), m, k)
+    tok, logit = pbg.int8_head_argmax(w, s, dev(x))
+    y = pbg.int8_head_gemv(w, s, dev(x)).cpu().numpy()
+    tok = tok.cpu().numpy()
+    for i in range(m):
+        assert tok[i] == int(np.argmax(y[i]))
+        assert logit.cpu().numpy()[i] == y[i, tok[i]]
+    # the chosen rows against the oracle
+    rows = torch.from_numpy(tok.astype(np.int64)).to("cuda:0")
+    w_rows = w[rows].cpu().numpy()
+    s_rows = s.cpu().numpy()[tok]
+    ref = oracle.int8_head_gemv(w_rows, s_rows, x)
+    b = head_bound(w_rows, s_rows, x)
+    for i in range(m):
+        assert abs(float(logit.cpu().numpy()[i]) - ref[i, i]) <= b[i, i]
+
+
+def test_embedding_gather_exact(pbg):
+    n, k = 777, 4100
+    table = synth.int8_full_range(20000, n, k)
+    s = synth.row_scales(20001, n)
+    tokens = np.array([0, 776, 5, 5, 300, -1, 777, 123], dtype=np.int32)
+    ref = oracle.embedding_gather(table, s, tokens)
+    out = pbg.int8_embedding_gather(dev(table), dev(s), dev(tokens)).cpu().numpy()
+    ok = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(out), ~ok)
+    assert np.array_equal(out[ok], ref[ok])
+
+
+def test_embedding_gather_full_table(pbg):
+    n, k = synth.HEAD_SHAPE
+    table = synth.head_weights_device(synth.SEED_HEAD + 1, n, k, "cuda:0")
+    s = synth.row_scales_device(synth.SEED_HEAD + 1, n, "cuda:0")
+    tokens = np.random.Generator(np.random.PCG64(21)).integers(0, n, size=64).astype(np.int32)
+    tokens[:2] = [0, n - 1]
+    out = pbg.int8_embedding_gather(table, s, dev(tokens)).cpu().numpy()
+    rows = torch.from_numpy(tokens.astype(np.int64)).to("cuda:0")
+    sub = table[rows].cpu().numpy()
+    ref = oracle.embedding_gather(sub, s.cpu().numpy()[tokens], np.arange(len(tokens)))
+    assert np.array_equal(out, ref)
