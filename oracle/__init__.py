@@ -24,6 +24,10 @@ What it computes (Neutrino-1 8B model page, English text on bittide):
   among equal maxima).
 * The int8 input embedding has a per-row scale and is read one row per token
   ("Where the bytes live"): the embedding of token t is s_t * w_t.
+* The feed-forward block is gated (SwiGLU) with three linears per layer
+  (geometry table): h = silu(gate x) * (up x), rounded to fp16, then down h.
+  The page names the gate but not its formula; silu(z) = z * sigmoid(z) is
+  the usual reading.
 
 Bit layout of one 32-bit word (little-endian uint32) holding 16 codes:
   code j (0..15) belongs to pair t = j // 2 and half h = j % 2;
@@ -48,7 +52,8 @@ any order; the only rounding is the final multiply by the scale.
 Parity pins: see tests/test_oracle.py (exhaustive single-word round trip,
 hand-written format words, the fp16 reading of the layout, brute force
 over all ternary rows for K <= 8 against exact rational sums, closed forms,
-exact integer matmul for the head, the row-sum and count invariants).
+exact integer matmul for the head, the row-sum and count invariants, silu at
+closed-form points and its Lambert-W minimum, an integer SwiGLU probe).
 """
 from __future__ import annotations
 
@@ -223,3 +228,35 @@ def embedding_gather(table: np.ndarray, scale: np.ndarray, tokens: np.ndarray) -
         if 0 <= t < n:
             out[i] = (np.float64(scale[t]) * table[t].astype(np.float64)).astype(np.float32)
     return out
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """z * sigmoid(z) in fp64, written so that neither branch overflows."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = z[pos] / (1.0 + np.exp(-z[pos]))
+    e = np.exp(z[~pos])
+    out[~pos] = z[~pos] * e / (1.0 + e)
+    return out
+
+
+def ffn_swiglu(gate_packed: np.ndarray, gate_scale: np.ndarray, up_packed: np.ndarray, up_scale: np.ndarray,
+               down_packed: np.ndarray, down_scale: np.ndarray, d_model: int, x: np.ndarray):
+    """The gated feed-forward block of one layer on M activation rows.
+
+    The geometry table of the Neutrino-1 8B model page gives the feed-forward
+    block as gated (SwiGLU) with three linears per layer. Read as usual:
+    g = gate x, u = up x (both ternary linears with per-row scales),
+    h = silu(g) * u, y = down h. h is the activation the down linear
+    consumes, so it is rounded once to fp16 like every other linear input.
+    Returns (h fp16 [m, d_ff], y fp64 [m, d_model]).
+    """
+    d_ff = gate_packed.shape[0]
+    if up_packed.shape[0] != d_ff or down_packed.shape[0] != d_model:
+        raise ValueError("gate and up are [d_ff, .], down is [d_model, .]")
+    g = ternary_gemm_small(gate_packed, gate_scale, d_model, x)
+    u = ternary_gemm_small(up_packed, up_scale, d_model, x)
+    h = (silu(g) * u).astype(np.float16)
+    y = ternary_gemm_small(down_packed, down_scale, d_ff, h)
+    return h, y

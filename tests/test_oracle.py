@@ -308,3 +308,127 @@ def test_embedding_rows_exact():
         for j in range(k):
             assert out[i, j] == np.float32(float(Fraction(float(s[t])) * int(table[t, j])))
     assert np.all(np.isnan(out[4:]))
+
+
+# --------------------------------------------------------------------------
+# Gated (SwiGLU) feed-forward block
+# --------------------------------------------------------------------------
+def test_silu_closed_forms():
+    """sigmoid(ln 3) = 3/4 and sigmoid(0) = 1/2 fix silu at three points; silu(z) - silu(-z) = z."""
+    l3 = math.log(3.0)
+    z = np.array([0.0, l3, -l3])
+    s = oracle.silu(z)
+    assert s[0] == 0.0
+    assert abs(s[1] - 0.75 * l3) <= 1e-15
+    assert abs(s[2] + 0.25 * l3) <= 1e-15
+    zz = np.random.default_rng(5).normal(0, 6, 1000)
+    np.testing.assert_allclose(oracle.silu(zz) - oracle.silu(-zz), zz, rtol=0, atol=1e-12)
+    big = np.array([40.0, 700.0, -40.0, -745.0, -800.0])
+    out = oracle.silu(big)
+    assert out[0] == 40.0 and out[1] == 700.0  # 1 + e^-40 rounds to 1 in fp64
+    assert abs(out[2]) < 1e-15 and abs(out[3]) < 1e-300 and out[4] == 0.0
+    assert np.all(np.isfinite(out))
+
+
+def test_silu_minimum_is_lambert_w():
+    """silu has its minimum value -W(1/e) at z = -1 - W(1/e) (W: Lambert's function, from scipy)."""
+    from scipy.special import lambertw
+
+    w = float(lambertw(math.exp(-1.0)).real)
+    z = np.linspace(-1.4, -1.1, 300001)
+    s = oracle.silu(z)
+    i = int(np.argmin(s))
+    assert abs(s[i] + w) < 1e-11
+    assert abs(z[i] - (-1.0 - w)) < 2e-6
+
+
+def _ffn_probe(seed: int, d_model: int, d_ff: int):
+    """Codes for which the block's result is known in integers.
+
+    x is +-1. Gate row r has |S_r| codes equal to sign(x_j) (or all negated),
+    so g_r = +-|S_r| with |S_r| >= 40 (scale 1). Up rows have at most 16
+    nonzero codes, so u_r is an integer in [-16, 16]. silu(g) is then g to
+    within g e^-g (positive rows) or below 1e-15 (negative rows), so
+    h = g * u exactly (|h| <= 2048 is fp16-exact) or 0.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.choice(np.array([-1.0, 1.0], dtype=np.float16), size=d_model)
+    sx = np.where(x > 0, 1, -1).astype(np.int8)
+    gate = np.zeros((d_ff, d_model), dtype=np.int8)
+    up = np.zeros((d_ff, d_model), dtype=np.int8)
+    h_exp = np.zeros(d_ff, dtype=np.int64)
+    for r in range(d_ff):
+        size = int(rng.integers(40, min(d_model, 120) + 1))
+        cols = rng.choice(d_model, size=size, replace=False)
+        neg = r % 5 == 3
+        gate[r, cols] = -sx[cols] if neg else sx[cols]
+        ucols = rng.choice(d_model, size=int(rng.integers(0, 17)), replace=False)
+        up[r, ucols] = rng.choice(np.array([-1, 1], dtype=np.int8), size=ucols.size)
+        u = int(np.dot(up[r].astype(np.int64), sx.astype(np.int64)))
+        h_exp[r] = 0 if neg else size * u
+    down = synth.ternary_codes(seed + 1, d_model, d_ff)
+    return x, gate, up, down, h_exp
+
+
+def test_ffn_integer_probe_exact():
+    """h = g * u exactly and y = s_d * (C_down @ h) in exact integer arithmetic."""
+    d_model, d_ff = 192, 136
+    x, gate, up, down, h_exp = _ffn_probe(41, d_model, d_ff)
+    one_f = np.ones(d_ff, dtype=np.float32)
+    s_d = synth.pow2_scales(42, d_model)
+    gp, _, _ = oracle.pack(gate)
+    upk, _, _ = oracle.pack(up)
+    dp, _, _ = oracle.pack(down)
+    h, y = oracle.ffn_swiglu(gp, one_f, upk, one_f, dp, s_d, d_model, x)
+    assert h.dtype == np.float16 and h.shape == (1, d_ff)
+    assert np.array_equal(h[0].astype(np.float64), h_exp.astype(np.float64))
+    assert np.count_nonzero(h_exp) > d_ff // 2
+    y_exp = (down.astype(np.int64) @ h_exp).astype(np.float64) * s_d.astype(np.float64)
+    assert np.array_equal(y[0], y_exp)
+
+
+def test_ffn_gate_is_the_silu_input():
+    """silu acts on the gate output, not on the up output: with g = ln 3 and u = 1, h = fp16(3/4 ln 3)."""
+    d_model, d_ff = 64, 4
+    x = np.zeros(d_model, dtype=np.float16)
+    x[0] = 1.0
+    gate = np.zeros((d_ff, d_model), dtype=np.int8)
+    up = np.zeros((d_ff, d_model), dtype=np.int8)
+    gate[:, 0] = 1
+    up[:, 0] = 1
+    gs = np.full(d_ff, math.log(3.0), dtype=np.float32)   # g = fp32(ln 3)
+    us = np.array([1.0, 2.0, 0.5, -1.0], dtype=np.float32)  # u
+    down = np.zeros((d_model, d_ff), dtype=np.int8)
+    down[0, :] = 1
+    h, y = oracle.ffn_swiglu(oracle.pack(gate)[0], gs, oracle.pack(up)[0], us, oracle.pack(down)[0],
+                             np.ones(d_model, dtype=np.float32), d_model, x)
+    want = np.float16(0.75 * math.log(3.0)) * us.astype(np.float64)
+    assert np.array_equal(h[0].astype(np.float64), want.astype(np.float16).astype(np.float64))
+    assert y[0, 0] == math.fsum(h[0].astype(np.float64)) and np.all(y[0, 1:] == 0)
+
+
+def test_ffn_zero_gate_or_up_gives_zero():
+    d_model, d_ff = 128, 70
+    x = synth.activations(43, 1, d_model)[0]
+    codes = synth.ternary_codes(44, d_ff, d_model)
+    zeros = np.zeros_like(codes)
+    down = synth.ternary_codes(45, d_model, d_ff)
+    s = synth.row_scales(46, d_ff)
+    sd = synth.row_scales(47, d_model)
+    for g, u in ((zeros, codes), (codes, zeros)):
+        h, y = oracle.ffn_swiglu(oracle.pack(g)[0], s, oracle.pack(u)[0], s, oracle.pack(down)[0], sd, d_model, x)
+        assert np.all(h == 0) and np.all(y == 0)
+
+
+def test_ffn_rows_independent():
+    """M activation rows give the rows of M separate calls."""
+    d_model, d_ff = 128, 80
+    x = synth.activations(48, 3, d_model)
+    g = oracle.pack(synth.ternary_codes(49, d_ff, d_model))[0]
+    u = oracle.pack(synth.ternary_codes(50, d_ff, d_model))[0]
+    d = oracle.pack(synth.ternary_codes(51, d_model, d_ff))[0]
+    sg, su, sd = synth.row_scales(52, d_ff), synth.row_scales(53, d_ff), synth.row_scales(54, d_model)
+    h, y = oracle.ffn_swiglu(g, sg, u, su, d, sd, d_model, x)
+    for m in range(3):
+        h1, y1 = oracle.ffn_swiglu(g, sg, u, su, d, sd, d_model, x[m])
+        assert np.array_equal(h1[0], h[m]) and np.array_equal(y1[0], y[m])
