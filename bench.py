@@ -1,17 +1,21 @@
 """Benchmark of the packed ternary GEMV path on one MI355X.
 
 Headline (one JSON line on stdout): achieved HBM GB/s of the feed-forward
-ternary GEMVs at M = 1 (gate and up 12288 x 4096, down 4096 x 12288; codes
-with 71 % zeros for gate/down in layers 1-3 and 62.63 % elsewhere, Neutrino-1 8B
-model page, "Inside the coded lane"). One step = one decoder layer's three FFN
-GEMVs on fresh activations; steps walk a pool of 36 distinct synthetic layers
-(1.37 GB of packed weights, far above the 256 MB Infinity Cache), so every
-step streams its weights from HBM.
+ternary linears at M = 1 (gate and up 12288 x 4096, down 4096 x 12288; codes
+with 71 % zeros for gate/down in layers 1-3 and 62.63 % elsewhere, Neutrino-1
+8B model page, "Inside the coded lane"), run the way the library runs a
+gated (SwiGLU) feed-forward block: ternary_ffn_swiglu = one launch for gate
+and up with the SwiGLU in its epilogue, then the down GEMV on its output. One
+step = one layer's block on fresh activations; steps walk a pool of 36
+distinct synthetic layers (1.37 GB of packed weights, far above the 256 MB
+Infinity Cache), so every step streams its weights from HBM.
 
-Also reported under "extra": microseconds per linear, per decoder layer (7
-linears) and per full decode step (36 layers + int8 head 151,936 x 4,096), the
-head alone, and the small-M (speculative verify) shapes, plus the streaming
-read ceiling of a plain copy (torch) at the same byte count.
+Also reported under "extra": the same three linears as three separate GEMV
+launches, microseconds per linear, per decoder layer (7 linears, and with the
+shared-input fusions) and per full decode step (36 layers + int8 head
+151,936 x 4,096), the head alone and with the fused greedy argmax, the
+small-M (speculative verify) shapes, and the streaming ceiling of a plain
+copy (torch) at the same byte count.
 """
 from __future__ import annotations
 
@@ -31,9 +35,8 @@ import synth  # noqa: E402
 
 METRIC = "achieved HBM GB/s (% of peak) for packed-ternary GEMV, M=1; µs per decoder layer"
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_ternary_gemv_ffn_m1.json")
-CHUNK = 12  # steps per replayed graph in the timed region
-KERNEL_SOURCES = ("packed_bit_gemv_amd/csrc/ternary.hip", "packed_bit_gemv_amd/csrc/pbg_device.hpp")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_swiglu_gate_up_m1.json")
+KERNEL_SOURCES = ("packed_bit_gemv_amd/csrc/ffn.hip", "packed_bit_gemv_amd/csrc/pbg_device.hpp")
 
 
 def log(*a):
@@ -43,6 +46,12 @@ def log(*a):
 def ternary_bytes(n: int, k: int, m: int = 1) -> int:
     """Algorithmic bytes of one call: packed words + fp32 scales + fp16 x + fp32 y."""
     return synth.words_bytes(n, k) + 4 * n + 2 * m * k + 4 * m * n
+
+
+def gate_up_bytes(d_ff: int, d_model: int) -> int:
+    """Algorithmic bytes of the gate|up + SwiGLU launch: both packed matrices,
+    both scale vectors, x once, h (fp16) out."""
+    return 2 * synth.words_bytes(d_ff, d_model) + 2 * 4 * d_ff + 2 * d_model + 2 * d_ff
 
 
 def head_bytes(n: int, k: int, m: int = 1) -> int:
@@ -208,43 +217,54 @@ def main():
         for p in ffn:
             linear(layer, p)
 
-    # ---- headline: FFN GEMVs at M = 1 ---------------------------------------
-    # Steps are replayed from HIP graphs: step i runs the gate, up and down
-    # GEMVs of layer i % L, so consecutive steps stream different weights from
-    # HBM. Runs of CHUNK steps that start at a multiple of CHUNK replay one
-    # graph of 3 * CHUNK launches; other steps replay a one-step graph, so
-    # exactly `steps` steps are timed. Events on the replay stream bracket the
-    # timed region.
-    chunk = CHUNK if L % CHUNK == 0 else 1
-    single = [capture(torch, lambda l=l: ffn_step(l)) for l in range(L)]
-    chunked = [capture(torch, lambda c=c: [ffn_step(c * chunk + j) for j in range(chunk)])
-               for c in range(L // chunk)]
+    h_ff = torch.empty(synth.FFN, dtype=torch.float16, device=device)
+    y_ff = torch.empty(synth.HIDDEN, dtype=torch.float32, device=device)
 
-    def replay_steps(first, count):
-        i = first
-        while i < first + count:
-            if chunk > 1 and i % chunk == 0 and i + chunk <= first + count:
-                chunked[(i % L) // chunk].replay()
-                i += chunk
-            else:
-                single[i % L].replay()
-                i += 1
+    def ffn_block(layer):
+        lay = model.layers[layer]
+        pbg.ternary_ffn_swiglu(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], lay["down"][0],
+                               lay["down"][1], xs[synth.HIDDEN][0], h_ff, y_ff)
 
+    def gate_up(layer):
+        lay = model.layers[layer]
+        pbg.ternary_swiglu_gate_up(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], synth.HIDDEN,
+                                   xs[synth.HIDDEN][0], h_ff)
+
+    # ---- headline: the FFN block at M = 1 ------------------------------------
+    # Step i runs the block of layer i % L, so consecutive steps stream
+    # different weights from HBM. The W warm-up steps are one replayed HIP
+    # graph; the K timed steps are one replay of a graph that holds exactly
+    # those K steps, bracketed by events on the replay stream.
+    W0, K0 = args.warmup, args.steps
+    warm = capture(torch, lambda: [ffn_block(i % L) for i in range(W0)]) if W0 > 0 else None
+    timed = capture(torch, lambda: [ffn_block((W0 + i) % L) for i in range(K0)])
     bytes_step = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)
-    replay_steps(0, args.warmup)
+    if warm is not None:
+        warm.replay()
     torch.cuda.synchronize()
     ev_start = torch.cuda.Event(enable_timing=True)
     ev_end = torch.cuda.Event(enable_timing=True)
     ev_start.record()
-    replay_steps(args.warmup, args.steps)
+    timed.replay()
     ev_end.record()
     torch.cuda.synchronize()
-    ms_step = ev_start.elapsed_time(ev_end) / args.steps
+    ms_step = ev_start.elapsed_time(ev_end) / K0
     value = bytes_step / (ms_step * 1e-3) / 1e9
-    avg_launch_us = ms_step * 1e3 / len(ffn)
-    achieved = bytes_step / len(ffn) / (avg_launch_us * 1e-6) / 1e9
-    log(f"ffn step {ms_step * 1e3:.3f} us, {value:.1f} GB/s; {avg_launch_us:.3f} us per launch")
-    del single, chunked
+    log(f"ffn block step {ms_step * 1e3:.3f} us, {value:.1f} GB/s")
+    del warm, timed
+
+    # dominant kernel of the step: the gate|up + SwiGLU launch, timed alone
+    # (a graph of L consecutive launches over the pool)
+    g = capture(torch, lambda: [gate_up(l) for l in range(L)])
+    gate_up_us = time_graphs(torch, [g], max(5, args.steps // 40), 1) * 1e3 / L
+    gu_bytes = gate_up_bytes(synth.FFN, synth.HIDDEN)
+    achieved = gu_bytes / (gate_up_us * 1e-6) / 1e9
+    del g
+
+    # the same three linears as three separate M = 1 GEMV launches
+    g = capture(torch, lambda: [ffn_step(l) for l in range(L)])
+    three_us = time_graphs(torch, [g], 5, 1) * 1e3 / L
+    del g
 
     # per-projection launch time: a graph of the same projection over all layers
     per_proj_us = {}
@@ -259,7 +279,10 @@ def main():
         if tr.get("kernel_hash") == kernel_hash():
             traffic = tr.get("bytes_per_launch")
 
-    extra = {"us_per_launch": {p: round(v, 3) for p, v in per_proj_us.items()},
+    extra = {"ffn_three_gemv_m1_us": round(three_us, 3),
+             "ffn_three_gemv_m1_GBs": round(bytes_step / (three_us * 1e-6) / 1e9, 1),
+             "swiglu_gate_up_us_per_launch": round(gate_up_us, 3),
+             "us_per_launch": {p: round(v, 3) for p, v in per_proj_us.items()},
              "GBs_per_launch": {p: round(ternary_bytes(*synth.SHAPES[p]) / (v * 1e-6) / 1e9, 1)
                                 for p, v in per_proj_us.items()},
              "layers_in_pool": L, "pool_bytes_packed": bytes_step * L}
@@ -327,41 +350,39 @@ def main():
             extra[f"head_argmax_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
             del g
 
-        # shared-input fusion: q|k|v and gate|up as one packed matrix each
-        # (row concatenation of packs with the same K is itself a pack)
+        # shared-input fusions: q|k|v as one packed matrix (row concatenation of
+        # packs with the same K is itself a pack), o, then the FFN block
         fused = []
         for l in range(L):
             lay = model.layers[l]
-            qkv = (torch.cat([lay[p][0] for p in ("q", "k", "v")]), torch.cat([lay[p][1] for p in ("q", "k", "v")]))
-            gu = (torch.cat([lay[p][0] for p in ("gate", "up")]), torch.cat([lay[p][1] for p in ("gate", "up")]))
-            fused.append((qkv, gu))
-        y_qkv = torch.empty(fused[0][0][0].shape[0], dtype=torch.float32, device=device)
-        y_gu = torch.empty(fused[0][1][0].shape[0], dtype=torch.float32, device=device)
-
-        def fused_ffn(l):
-            (gp, gs) = fused[l][1]
-            pbg.ternary_gemv(gp, gs, synth.HIDDEN, xs[synth.HIDDEN][0], y_gu)
-            linear(l, "down")
+            fused.append((torch.cat([lay[p][0] for p in ("q", "k", "v")]),
+                          torch.cat([lay[p][1] for p in ("q", "k", "v")])))
+        y_qkv = torch.empty(fused[0][0].shape[0], dtype=torch.float32, device=device)
 
         def fused_layer(l):
-            (qp, qs) = fused[l][0]
+            qp, qs = fused[l]
             pbg.ternary_gemv(qp, qs, synth.HIDDEN, xs[synth.HIDDEN][0], y_qkv)
             linear(l, "o")
-            fused_ffn(l)
+            ffn_block(l)
 
-        ffn_bytes = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)
-        graphs = [capture(torch, lambda l=l: fused_ffn(l)) for l in range(L)]
+        graphs = [capture(torch, lambda l=l: fused_layer(l)) for l in range(L)]
         ms = time_graphs(torch, graphs, K, W)
-        extra["ffn_fused_m1_us"] = round(ms * 1e3, 3)
-        extra["ffn_fused_m1_GBs"] = round(ffn_bytes / (ms * 1e-3) / 1e9, 1)
-        g = capture(torch, lambda: [fused_ffn(l) for l in range(L)])
-        ms = time_graphs(torch, [g], 5, 1) / L
-        extra["ffn_fused_m1_us_36_per_graph"] = round(ms * 1e3, 3)
-        extra["ffn_fused_m1_GBs_36_per_graph"] = round(ffn_bytes / (ms * 1e-3) / 1e9, 1)
-        g = capture(torch, lambda: [fused_layer(l) for l in range(L)])
-        ms = time_graphs(torch, [g], 5, 1) / L
         extra["layer_fused_m1_us"] = round(ms * 1e3, 3)
         extra["layer_fused_m1_GBs"] = round(layer_bytes / (ms * 1e-3) / 1e9, 1)
+        g = capture(torch, lambda: [fused_layer(l) for l in range(L)])
+        ms = time_graphs(torch, [g], 5, 1) / L
+        extra["layer_fused_m1_us_36_per_graph"] = round(ms * 1e3, 3)
+        extra["layer_fused_m1_GBs_36_per_graph"] = round(layer_bytes / (ms * 1e-3) / 1e9, 1)
+
+        def decode_fused():
+            for l in range(L):
+                fused_layer(l)
+            head(1)
+
+        g = capture(torch, decode_fused)
+        ms = time_graphs(torch, [g], 5, 1)
+        extra["decode_step_fused_m1_us"] = round(ms * 1e3, 1)
+        extra["decode_step_fused_m1_GBs"] = round(dec_bytes / (ms * 1e-3) / 1e9, 1)
         del graphs, g, fused
 
         # streaming-read ceiling at the gate byte count: torch copy over a pool
@@ -393,6 +414,7 @@ def main():
             "m": 1,
             "layers_in_pool": L,
             "us_per_step": round(ms_step * 1e3, 3),
+            "path": "ternary_ffn_swiglu: gate|up + SwiGLU in one launch, then the down GEMV on its fp16 output",
         },
         "roofline": {
             "bound": "hbm",
@@ -401,9 +423,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "ternary_gemv_kernel",
-            "avg_launch_us": round(avg_launch_us, 3),
-            "launch_us_note": "timed-region time / launches; HIP graphs of 12 steps (36 launches), gaps included",
+            "kernel": "swiglu_gate_up_kernel",
+            "bytes_per_launch": gu_bytes,
+            "avg_launch_us": round(gate_up_us, 3),
+            "launch_us_note": "HIP events around a replayed graph of 36 consecutive launches over the pool, "
+                              "divided by 36 (inter-launch gaps included)",
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
         "extra": extra,

@@ -168,6 +168,48 @@ int int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, 
 int int8_embedding_gather(const int8_t* table, const float* scale, int64_t n, int64_t k, const int32_t* tokens,
                           int64_t m, float* out, hipStream_t stream);
 
+/* Largest d_model of ternary_ffn_swiglu (one 4,096-column slice per row). */
+#define PBG_FFN_MAX_MODEL 4096
+
+/*
+ * ternary_swiglu_gate_up - the first half of ternary_ffn_swiglu on its own:
+ * h[j] = fp16(silu(g[j]) * u[j]) with g = gate x and u = up x, in one launch
+ * that reads gate and up together; g and u never reach memory.
+ * Source: as ternary_ffn_swiglu. Arguments, layouts, alignment and limits
+ * are those of ternary_ffn_swiglu.
+ */
+int ternary_swiglu_gate_up(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                           const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
+                           hipStream_t stream);
+
+/*
+ * ternary_ffn_swiglu - the gated feed-forward block of one layer for one
+ * activation row:
+ *   g = gate x, u = up x              (ternary linears, d_ff x d_model)
+ *   h[j] = fp16(silu(g[j]) * u[j])    (silu(z) = z / (1 + exp(-z)); rounded
+ *                                      to nearest even, overflow to +-inf)
+ *   y = down h                        (ternary linear, d_model x d_ff)
+ * Source: Neutrino-1 8B model page, geometry table (feed-forward gated by
+ * SwiGLU, three linears per layer; widths 4,096 and 12,288) and "Where the
+ * bytes live" (per-row scales). The page does not write the gate out; silu
+ * on the gate output times the up output is the usual SwiGLU.
+ * Two launches on `stream`: ternary_swiglu_gate_up (gate and up together,
+ * SwiGLU in the epilogue), then ternary_gemv of down on h.
+ *
+ *   gate_packed, up_packed  [d_ff][pbg_words_per_row(d_model)] uint32, 16-byte
+ *                           aligned; gate_scale, up_scale [d_ff] fp32
+ *   down_packed             [d_model][pbg_words_per_row(d_ff)] uint32, 16-byte
+ *                           aligned; down_scale [d_model] fp32
+ *   x        [d_model] fp16 bits, 16-byte aligned
+ *   h        [d_ff] fp16 bits out, 16-byte aligned: the down linear's input
+ *   y        [d_model] fp32 out
+ *   8 <= d_model <= PBG_FFN_MAX_MODEL with d_model % 8 == 0;
+ *   1 <= d_ff <= PBG_MAX_N.
+ */
+int ternary_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                       const float* up_scale, const uint32_t* down_packed, const float* down_scale, int64_t d_model,
+                       int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

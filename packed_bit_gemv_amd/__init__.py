@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     int8_head_gemv,
     lib,
     pack_ternary,
+    ternary_ffn_swiglu,
+    ternary_swiglu_gate_up,
     ternary_gemm_small,
     ternary_gemv,
     words_per_row,
@@ -23,6 +25,8 @@ __all__ = [
     "int8_head_gemv",
     "lib",
     "pack_ternary",
+    "ternary_ffn_swiglu",
+    "ternary_swiglu_gate_up",
     "ternary_gemm_small",
     "ternary_gemv",
     "words_per_row",

@@ -32,6 +32,8 @@ _SIGNATURES = {
     "int8_head_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "int8_head_argmax": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _vp, _vp]),
     "int8_embedding_gather": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "ternary_swiglu_gate_up": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "ternary_ffn_swiglu": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -237,3 +239,67 @@ def int8_embedding_gather(table: torch.Tensor, scale: torch.Tensor, tokens: torc
                                      out.data_ptr(), _stream(table))
     _check("int8_embedding_gather", rc)
     return out
+
+
+def ternary_swiglu_gate_up(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
+                           d_model: int, x: torch.Tensor, h: torch.Tensor | None = None) -> torch.Tensor:
+    """h = fp16(silu(gate x) * up x) in one launch; gate, up packed [d_ff, words_per_row(d_model)]."""
+    for t, name in ((gate, "gate"), (up, "up")):
+        _dev(t, name, torch.int32)
+    for t, name in ((gate_scale, "gate_scale"), (up_scale, "up_scale")):
+        _dev(t, name, torch.float32)
+    _dev(x, "x", torch.float16)
+    d_ff = gate.shape[0]
+    if gate.dim() != 2 or tuple(up.shape) != tuple(gate.shape) or gate.shape[1] != words_per_row(d_model):
+        raise ValueError(f"gate and up must be [d_ff, {words_per_row(d_model)}]")
+    if tuple(gate_scale.shape) != (d_ff,) or tuple(up_scale.shape) != (d_ff,):
+        raise ValueError("scales must be [d_ff]")
+    if tuple(x.shape) != (d_model,):
+        raise ValueError(f"x must be [{d_model}]")
+    if h is None:
+        h = torch.empty((d_ff,), dtype=torch.float16, device=gate.device)
+    _dev(h, "h", torch.float16)
+    if tuple(h.shape) != (d_ff,):
+        raise ValueError("h must be [d_ff]")
+    rc = lib().ternary_swiglu_gate_up(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                      d_model, d_ff, x.data_ptr(), h.data_ptr(), _stream(gate))
+    _check("ternary_swiglu_gate_up", rc)
+    return h
+
+
+def ternary_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
+                       down: torch.Tensor, down_scale: torch.Tensor, x: torch.Tensor,
+                       h: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """Gated feed-forward block: h = fp16(silu(gate x) * up x), y = down h.
+
+    gate, up: packed [d_ff, words_per_row(d_model)]; down: packed [d_model, words_per_row(d_ff)];
+    x fp16 [d_model]. Returns (h fp16 [d_ff], y fp32 [d_model]).
+    """
+    for t, name in ((gate, "gate"), (up, "up"), (down, "down")):
+        _dev(t, name, torch.int32)
+    for t, name in ((gate_scale, "gate_scale"), (up_scale, "up_scale"), (down_scale, "down_scale")):
+        _dev(t, name, torch.float32)
+    _dev(x, "x", torch.float16)
+    d_ff, d_model = gate.shape[0], down.shape[0]
+    if gate.dim() != 2 or tuple(up.shape) != tuple(gate.shape) or gate.shape[1] != words_per_row(d_model):
+        raise ValueError(f"gate and up must be [d_ff, {words_per_row(d_model)}]")
+    if down.dim() != 2 or down.shape[1] != words_per_row(d_ff):
+        raise ValueError(f"down must be [d_model, {words_per_row(d_ff)}]")
+    if tuple(gate_scale.shape) != (d_ff,) or tuple(up_scale.shape) != (d_ff,) or tuple(down_scale.shape) != (d_model,):
+        raise ValueError("scales must be [d_ff], [d_ff], [d_model]")
+    if tuple(x.shape) != (d_model,):
+        raise ValueError(f"x must be [{d_model}]")
+    dev = gate.device
+    if h is None:
+        h = torch.empty((d_ff,), dtype=torch.float16, device=dev)
+    if y is None:
+        y = torch.empty((d_model,), dtype=torch.float32, device=dev)
+    _dev(h, "h", torch.float16)
+    _dev(y, "y", torch.float32)
+    if tuple(h.shape) != (d_ff,) or tuple(y.shape) != (d_model,):
+        raise ValueError("h must be [d_ff] and y [d_model]")
+    rc = lib().ternary_ffn_swiglu(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                  down.data_ptr(), down_scale.data_ptr(), d_model, d_ff, x.data_ptr(), h.data_ptr(),
+                                  y.data_ptr(), _stream(gate))
+    _check("ternary_ffn_swiglu", rc)
+    return h, y

@@ -98,4 +98,37 @@ int int8_embedding_gather(const int8_t* table, const float* scale, int64_t n, in
   return finish(pbg::launch_embedding_gather(table, scale, n, k, tokens, m, out, stream));
 }
 
+namespace {
+bool bad_ffn(int64_t d_model, int64_t d_ff) {
+  return d_model < 8 || d_model > PBG_FFN_MAX_MODEL || d_model % 8 != 0 || bad_nk(d_ff, d_model);
+}
+}  // namespace
+
+int ternary_swiglu_gate_up(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                           const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
+                           hipStream_t stream) {
+  if (!gate_packed || !gate_scale || !up_packed || !up_scale || !x || !h) return PBG_ERR_NULL;
+  if (bad_ffn(d_model, d_ff)) return PBG_ERR_SHAPE;
+  if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(gate_scale, 4) ||
+      misaligned(up_scale, 4) || misaligned(x, 16) || misaligned(h, 16))
+    return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_swiglu_gate_up(gate_packed, gate_scale, up_packed, up_scale, d_model, d_ff, x, h, stream));
+}
+
+int ternary_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                       const float* up_scale, const uint32_t* down_packed, const float* down_scale, int64_t d_model,
+                       int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream) {
+  if (!gate_packed || !gate_scale || !up_packed || !up_scale || !down_packed || !down_scale || !x || !h || !y)
+    return PBG_ERR_NULL;
+  if (bad_ffn(d_model, d_ff)) return PBG_ERR_SHAPE;
+  if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(down_packed, 16) ||
+      misaligned(gate_scale, 4) || misaligned(up_scale, 4) || misaligned(down_scale, 4) || misaligned(x, 16) ||
+      misaligned(h, 16) || misaligned(y, 4))
+    return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_ffn_swiglu(gate_packed, gate_scale, up_packed, up_scale, down_packed, down_scale, d_model,
+                                       d_ff, x, h, y, stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,147 @@
+// ternary_ffn_swiglu: the gated feed-forward block of one layer at M = 1
+// (Neutrino-1 8B model page: geometry table, gated SwiGLU feed-forward with
+// three linears; per-row scales, "Where the bytes live").
+//
+//   launch 1   g = gate x, u = up x, h = fp16(silu(g) * u)  -> h
+//   launch 2   y = down h (the M = 1 GEMV of ternary.hip)   -> y
+//
+// Launch 1 reads gate and up (same K, same x) in one pass and forms h in its
+// epilogue, so the gate and up outputs never reach memory. A single
+// persistent launch with a grid-wide barrier between the two phases was
+// measured slower on gfx950: the barrier, the exchange of h through memory
+// and the down decode after the barrier cost more than the second launch.
+//
+// Work split of launch 1: a wave owns R consecutive row pairs (gate row r and
+// up row r) and reads 16-byte chunk `lane` (64 codes) of each; x is staged
+// through LDS like the M = 1 GEMV. The 2R row sums are reduced four at a time
+// across the wave, read back as uniform values, and lane 0 writes the R fp16
+// results with one store.
+#include "pbg_device.hpp"
+#include "pbg_internal.hpp"
+
+namespace pbg {
+namespace {
+
+constexpr int kPairs = 2;      // row pairs per wave
+constexpr int kFfnWaves = 4;   // waves per workgroup
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+template <int R, int G>
+__global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
+    const uint4* __restrict__ gate, const float* __restrict__ gate_scale, const uint4* __restrict__ up,
+    const float* __restrict__ up_scale, int64_t d_model, int64_t d_ff, int64_t chunks, const uint16_t* x,
+    uint16_t* __restrict__ h) {
+  static_assert(R == 1 || R == 2 || R == 4, "R pairs fill whole reductions");
+  constexpr int kThreads = G * kWave;
+  constexpr int kX = kWave * 8;  // 16-byte activation groups of one 4,096-column slice
+  constexpr int kRed = (2 * R + 3) / 4;
+  __shared__ uint4 buf[kX];      // group (c, q) at q * 64 + c
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t groups = d_model / 8;
+  const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * G + wave) * R;  // first row pair
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+
+  // activations first, then every weight load of the wave
+  constexpr int kXPer = (kX + kThreads - 1) / kThreads;
+  uint4 xv[kXPer];
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int gi = threadIdx.x + i * kThreads;
+    xv[i] = xg[gi < groups ? gi : 0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");  // activation loads queue ahead of the weight loads
+  __builtin_amdgcn_sched_barrier(0);
+  const int64_t cl = lane < chunks ? lane : chunks - 1;  // lanes past the row reread its last chunk (x is 0 there)
+  uint4 wg[R], wu[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int64_t r = r0 + i < d_ff ? r0 + i : d_ff - 1;
+    wg[i] = load_nt(gate + r * chunks + cl);
+    wu[i] = load_nt(up + r * chunks + cl);
+  }
+  const int64_t rs = r0 + (lane < R ? lane : 0);
+  const float sg = gate_scale[rs < d_ff ? rs : d_ff - 1];
+  const float su = up_scale[rs < d_ff ? rs : d_ff - 1];
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int gi = threadIdx.x + i * kThreads;
+    if (gi < kX) buf[(gi & 7) * kWave + (gi >> 3)] = gi < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  uint32_t xp[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = buf[q * kWave + lane];
+    xp[4 * q + 0] = v.x;
+    xp[4 * q + 1] = v.y;
+    xp[4 * q + 2] = v.z;
+    xp[4 * q + 3] = v.w;
+  }
+
+  float acc[4 * kRed];  // gate sums of the R pairs, then their up sums
+#pragma unroll
+  for (int i = 0; i < 4 * kRed; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    acc[i] = chunk_dot(wg[i], xp, 0.0f);
+    acc[R + i] = chunk_dot(wu[i], xp, 0.0f);
+  }
+  float red[kRed];
+#pragma unroll
+  for (int q = 0; q < kRed; ++q) red[q] = wave_reduce4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+
+  constexpr int kSlotLane[4] = {0, 32, 16, 48};  // lane holding operand 0..3 of wave_reduce4
+  uint32_t bits[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const float g = as_f32(__builtin_amdgcn_readlane(as_u32(red[i / 4]), kSlotLane[i % 4]));
+    const float u = as_f32(__builtin_amdgcn_readlane(as_u32(red[(R + i) / 4]), kSlotLane[(R + i) % 4]));
+    const float gs = as_f32(__builtin_amdgcn_readlane(as_u32(sg), i));
+    const float us = as_f32(__builtin_amdgcn_readlane(as_u32(su), i));
+    const float hv = silu(g * (gs * kCodeUnitInv)) * (u * (us * kCodeUnitInv));
+    bits[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
+  }
+  if (lane == 0) {
+    if (r0 + R <= d_ff) {
+      if constexpr (R == 1) {
+        h[r0] = static_cast<uint16_t>(bits[0]);
+      } else if constexpr (R == 2) {
+        *reinterpret_cast<uint32_t*>(h + r0) = bits[0] | (bits[1] << 16);
+      } else {
+        *reinterpret_cast<uint2*>(h + r0) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        if (r0 + i < d_ff) h[r0 + i] = static_cast<uint16_t>(bits[i]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_gate_up(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                 const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
+                                 hipStream_t stream) {
+  constexpr int64_t kRowsPerBlock = static_cast<int64_t>(kPairs) * kFfnWaves;
+  const dim3 grid(static_cast<unsigned>((d_ff + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((swiglu_gate_up_kernel<kPairs, kFfnWaves>), grid, dim3(kFfnWaves * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(gate), gate_scale, reinterpret_cast<const uint4*>(up), up_scale,
+                     d_model, d_ff, words_per_row(d_model) / 4, x, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_swiglu(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                             const float* up_scale, const uint32_t* down, const float* down_scale, int64_t d_model,
+                             int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream) {
+  const hipError_t e = launch_swiglu_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
+  if (e != hipSuccess) return e;
+  return launch_ternary_gemv(down, down_scale, d_model, d_ff, h, y, stream);
+}
+
+}  // namespace pbg

@@ -36,6 +36,55 @@ __device__ __forceinline__ float word_dot(uint32_t w, const uint32_t* xp, float 
   return acc;
 }
 
+// Two words shifted left by S in one 64-bit shift (v_lshlrev_b64 issues at the
+// cost of a 32-bit shift). For S <= 14 the bits carried from the low word into
+// the high word land below bit S, where kPairMask clears them, so both halves
+// decode exactly as separate 32-bit shifts would.
+template <int S>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+  static_assert(S > 0 && S <= 14, "carried bits must stay below the code fields");
+  uint64_t r;
+  asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(v));
+  return r;
+}
+
+// Operands t of the words (w0, w1) packed as w1:w0.
+template <int T>
+__device__ __forceinline__ void pair_ops(uint64_t w, uint32_t& op0, uint32_t& op1) {
+  if constexpr (T == 0) {
+    op0 = static_cast<uint32_t>(w) & kPairMask;
+    op1 = static_cast<uint32_t>(w >> 32) & kPairMask;
+  } else {
+    const uint64_t s = shl64<2 * T>(w);
+    op0 = static_cast<uint32_t>(s) & kPairMask;
+    op1 = static_cast<uint32_t>(s >> 32) & kPairMask;
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void chunk_ops(uint64_t lo, uint64_t hi, uint32_t (&op)[4][8]) {
+  pair_ops<T>(lo, op[0][T], op[1][T]);
+  pair_ops<T>(hi, op[2][T], op[3][T]);
+  if constexpr (T < 7) chunk_ops<T + 1>(lo, hi, op);
+}
+
+// Sum over one 16-byte chunk (4 words, 64 codes) against 32 activation pairs.
+// The four words feed four independent accumulators, interleaved so that a
+// single wave per SIMD still keeps the dot unit busy.
+__device__ __forceinline__ float chunk_dot(const uint4& w, const uint32_t* xp, float acc) {
+  uint32_t op[4][8];
+  chunk_ops<0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, op);
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    a0 = dot2(op[0][t], xp[t], a0);
+    a1 = dot2(op[1][t], xp[8 + t], a1);
+    a2 = dot2(op[2][t], xp[16 + t], a2);
+    a3 = dot2(op[3][t], xp[24 + t], a3);
+  }
+  return acc + ((a0 + a1) + (a2 + a3));
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte load marked non-temporal (streamed once, not kept in the caches).

@@ -24,6 +24,14 @@ hipError_t launch_int8_head_argmax(const int8_t* w, const float* scale, int64_t 
 hipError_t launch_embedding_gather(const int8_t* table, const float* scale, int64_t n, int64_t k,
                                    const int32_t* tokens, int64_t m, float* out, hipStream_t stream);
 
+hipError_t launch_swiglu_gate_up(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                 const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
+                                 hipStream_t stream);
+
+hipError_t launch_ffn_swiglu(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                             const float* up_scale, const uint32_t* down, const float* down_scale, int64_t d_model,
+                             int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream);
+
 // Workgroups one embedding gather launches (the grid must stay below 2^31 / 256).
 int64_t embedding_blocks(int64_t m, int64_t k);
 

@@ -20,29 +20,6 @@ namespace {
 constexpr int kRowsPerWave = 4;  // small-M kernel
 constexpr int kGemvWaves = 4;
 
-// Sum over one 16-byte chunk (4 words, 64 codes) against 32 activation pairs.
-// The four words feed four independent accumulators, interleaved so that a
-// single wave per SIMD still keeps the dot unit busy.
-__device__ __forceinline__ float chunk_dot(const uint4& w, const uint32_t* xp, float acc) {
-  uint32_t op[4][8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    op[0][t] = code_pair(w.x, t);
-    op[1][t] = code_pair(w.y, t);
-    op[2][t] = code_pair(w.z, t);
-    op[3][t] = code_pair(w.w, t);
-  }
-  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    a0 = dot2(op[0][t], xp[t], a0);
-    a1 = dot2(op[1][t], xp[8 + t], a1);
-    a2 = dot2(op[2][t], xp[16 + t], a2);
-    a3 = dot2(op[3][t], xp[24 + t], a3);
-  }
-  return acc + ((a0 + a1) + (a2 + a3));
-}
-
 // M = 1, fast path: k % 8 == 0, x 16-byte aligned and at most 4 K-slices of
 // 4,096 columns (one per wave of a row group). A workgroup holds G row
 // groups x SW K-slices; wave (g, s) owns R consecutive rows and the 16-byte

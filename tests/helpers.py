@@ -66,3 +66,51 @@ def read_key_values(name):
             key, val = (p.strip() for p in line.split("="))
             out[key] = int(val)
     return out
+
+
+def ffn_probe(seed: int, d_model: int, d_ff: int):
+    """Integer probe of the gated feed-forward block (d_model a multiple of 64).
+
+    x is +-1. Gate row r has size_r in [40, 120] nonzero codes, at columns
+    (37 r + 7 t) mod d_model, equal to sign(x_j) (negated on rows r = 3 mod 5),
+    so g_r = +-size_r exactly with scale 1. Up row r has at most 16 codes +-1
+    at columns (13 r + 11 t + 5) mod d_model, so u_r is an integer in
+    [-16, 16]. For g >= 40, 1 + e^-g rounds to 1 in fp32 and fp64 alike, so
+    silu(g) * u = g * u; for g <= -40 the product is below 1e-15 and rounds to
+    0 in fp16. Returns (x fp16, gate int8, up int8, h int64).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.choice(np.array([-1.0, 1.0]), size=d_model).astype(np.float16)
+    sx = np.where(x > 0, 1, -1).astype(np.int64)
+    r = np.arange(d_ff)
+    size = rng.integers(40, min(d_model, 120) + 1, size=d_ff)
+    usize = rng.integers(0, 17, size=d_ff)
+    neg = (r % 5) == 3
+    t = np.arange(120)
+    cols = (37 * r[:, None] + 7 * t[None, :]) % d_model
+    mask = t[None, :] < size[:, None]
+    rows = np.broadcast_to(r[:, None], cols.shape)
+    sign = np.where(neg, -1, 1)[:, None]
+    gate = np.zeros((d_ff, d_model), dtype=np.int8)
+    gate[rows[mask], cols[mask]] = (np.broadcast_to(sign, cols.shape) * sx[cols])[mask].astype(np.int8)
+    tu = np.arange(16)
+    ucols = (13 * r[:, None] + 11 * tu[None, :] + 5) % d_model
+    umask = tu[None, :] < usize[:, None]
+    usign = rng.choice(np.array([-1, 1]), size=ucols.shape)
+    up = np.zeros((d_ff, d_model), dtype=np.int8)
+    urows = np.broadcast_to(r[:, None], ucols.shape)
+    up[urows[umask], ucols[umask]] = usign[umask].astype(np.int8)
+    u = np.where(umask, usign * sx[ucols], 0).sum(axis=1)
+    h = np.where(neg, 0, size * u).astype(np.int64)
+    return x, gate, up, h
+
+
+def swiglu_h_bound(silu_g: np.ndarray, u: np.ndarray, tg: np.ndarray, tu: np.ndarray) -> np.ndarray:
+    """Bound on |h - h_ref| for h = fp16(silu(g) * u) when the kernel's g and u
+    are within tg and tu of the exact values: silu has slope at most 1.1, the
+    fp32 exp and divide add at most 1e-6 relative, and two fp16 roundings of
+    values that close differ by at most their distance plus one fp16 ulp."""
+    a = 1.1 * tg * (np.abs(u) + tu) + np.abs(silu_g) * tu + 1e-6 * np.abs(silu_g * u)
+    mag = np.abs(silu_g * u) + a
+    ulp = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(mag, 2.0 ** -14))) - 10), 2.0 ** -24)
+    return a + ulp

@@ -115,3 +115,20 @@ def test_strerror_is_static():
     lib = binding.lib()
     a = ctypes.cast(lib.pbg_strerror(-1), ctypes.c_char_p)
     assert a.value == b"a required pointer is NULL"
+
+
+@no_gpu_only
+def test_ffn_validation():
+    lib = binding.lib()
+    p6 = [GOOD] * 6
+    assert lib.ternary_ffn_swiglu(None, *p6[1:], 4096, 12288, GOOD, GOOD, GOOD, None) == -1
+    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD, GOOD, None, None) == -1
+    for dm, dff in ((0, 12288), (4096 + 8, 12288), (100, 12288), (4, 12288), (4096, 0), (4096, 2 ** 24 + 1)):
+        assert lib.ternary_ffn_swiglu(*p6, dm, dff, GOOD, GOOD, GOOD, None) == -2
+    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD + 8, GOOD, GOOD, None) == -3   # x
+    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD, GOOD + 2, GOOD, None) == -3   # h
+    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD, GOOD, GOOD + 2, None) == -3   # y
+    assert lib.ternary_ffn_swiglu(GOOD + 4, *p6[1:], 4096, 12288, GOOD, GOOD, GOOD, None) == -3
+    assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, None, None) == -1
+    assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4100, 12288, GOOD, GOOD, None) == -2
+    assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, GOOD + 2, None) == -3
