@@ -144,11 +144,19 @@ int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, co
  * plain greedy stream) and "Where the bytes live" (int8 head).
  *
  *   w, scale, x, m  as int8_head_gemv (1 <= m <= 8); logits must be finite
- *   keys    [m] uint64 device workspace, 8-byte aligned (cleared by the call)
+ *   keys    [m * PBG_ARGMAX_KEYS_PER_ROW] uint64 device workspace, 8-byte
+ *           aligned, owned by the caller and all zero before the first call
+ *           (e.g. one zero fill at allocation). Partial maxima of a row sit
+ *           in separate 128-byte lines so that workgroups do not queue on one
+ *           address; the call leaves the entries it used at zero again, so
+ *           the workspace stays ready. Calls that overlap in time need
+ *           separate workspaces.
  *   token   [m] int32 out, 4-byte aligned
  *   logit   [m] fp32 out, 4-byte aligned, or NULL
  * The result does not depend on the order in which workgroups finish.
  */
+#define PBG_ARGMAX_KEYS_PER_ROW 4096
+
 int int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                      uint64_t* keys, int32_t* token, float* logit, hipStream_t stream);
 

@@ -16,6 +16,7 @@ import torch
 from .build import LIB_PATH
 
 PBG_ERR_CODE = -4
+ARGMAX_KEYS_PER_ROW = 4096  # PBG_ARGMAX_KEYS_PER_ROW
 
 _c_int = ctypes.c_int
 _c_i64 = ctypes.c_int64
@@ -194,7 +195,11 @@ def int8_head_gemv(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor,
 
 def int8_head_argmax(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, keys: torch.Tensor | None = None,
                      token: torch.Tensor | None = None, logit: torch.Tensor | None = None):
-    """Greedy token per activation row: (token int32 [m], logit fp32 [m]); keys is an int64 [m] workspace."""
+    """Greedy token per activation row: (token int32 [m], logit fp32 [m]).
+
+    keys is an int64 workspace of at least m * ARGMAX_KEYS_PER_ROW entries, zero before its first
+    use and left zero by every call (a zeroed one is allocated if not given).
+    """
     _dev(w, "w", torch.int8)
     _dev(scale, "scale", torch.float32)
     _dev(x, "x", torch.float16)
@@ -204,7 +209,7 @@ def int8_head_argmax(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, keys
     m = x.shape[0]
     dev = w.device
     if keys is None:
-        keys = torch.empty((m,), dtype=torch.int64, device=dev)
+        keys = torch.zeros((m * ARGMAX_KEYS_PER_ROW,), dtype=torch.int64, device=dev)
     if token is None:
         token = torch.empty((m,), dtype=torch.int32, device=dev)
     if logit is None:
@@ -212,8 +217,8 @@ def int8_head_argmax(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, keys
     _dev(keys, "keys", torch.int64)
     _dev(token, "token", torch.int32)
     _dev(logit, "logit", torch.float32)
-    if keys.numel() != m or token.numel() != m or logit.numel() != m:
-        raise ValueError("keys, token and logit hold m entries")
+    if keys.numel() < m * ARGMAX_KEYS_PER_ROW or token.numel() != m or logit.numel() != m:
+        raise ValueError("keys holds m * ARGMAX_KEYS_PER_ROW entries, token and logit m")
     rc = lib().int8_head_argmax(w.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, keys.data_ptr(),
                                 token.data_ptr(), logit.data_ptr(), _stream(w))
     _check("int8_head_argmax", rc)

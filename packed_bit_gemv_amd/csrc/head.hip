@@ -6,6 +6,7 @@
 // turned into the fp16 value b exactly: the byte, biased to b + 128, becomes
 // the low mantissa byte of fp16 0x64xx = 1024 + (b + 128), and one packed fp16
 // subtraction of 1152 leaves b. v_dot2 then accumulates w * x in fp32.
+#include "packed_bit_gemv.h"
 #include "pbg_device.hpp"
 #include "pbg_internal.hpp"
 
@@ -14,6 +15,20 @@ namespace {
 
 constexpr int kHeadRows = 4;
 constexpr int kHeadWaves = 4;
+
+// Greedy-argmax keys of one activation row are spread over kArgmaxBins bins
+// on separate 128-byte lines (workgroup b uses bin b % kArgmaxBins): device
+// atomics on one address serialise at the memory side (about 10 ns each), so
+// ten thousand workgroups on one key would take as long as the head itself.
+// The bins are zero between calls: the caller zeroes the workspace once and
+// the finishing kernel clears every bin it has read.
+constexpr int kArgmaxBins = 256;
+constexpr int kArgmaxStride = 16;  // keys between bins (128 bytes)
+static_assert(kArgmaxBins * kArgmaxStride == PBG_ARGMAX_KEYS_PER_ROW, "workspace layout");
+
+__device__ __forceinline__ unsigned long long* argmax_bin(unsigned long long* keys, int row) {
+  return keys + (static_cast<int64_t>(row) * kArgmaxBins + blockIdx.x % kArgmaxBins) * kArgmaxStride;
+}
 
 // Four int8 weights (one dword) -> two fp16 pairs (w0, w1), (w2, w3).
 __device__ __forceinline__ void int8x4_to_half2x2(uint32_t v, uint32_t& lo, uint32_t& hi) {
@@ -92,7 +107,7 @@ __global__ __launch_bounds__(kHeadWaves* kWave) void int8_head_kernel(const int8
   }
   if constexpr (AM) {
     __syncthreads();
-    if (threadIdx.x < M) atomicMax(&keys[threadIdx.x], wg_key[threadIdx.x]);
+    if (threadIdx.x < M) atomicMax(argmax_bin(keys, threadIdx.x), wg_key[threadIdx.x]);
   }
 }
 
@@ -234,7 +249,7 @@ __global__ __launch_bounds__(SW* G* kWave) void int8_head_fast_kernel(const int8
   }
   if constexpr (AM) {
     __syncthreads();
-    if (threadIdx.x < M) atomicMax(&keys[threadIdx.x], wg_key[threadIdx.x]);
+    if (threadIdx.x < M) atomicMax(argmax_bin(keys, threadIdx.x), wg_key[threadIdx.x]);
   }
 }
 
@@ -358,7 +373,7 @@ __global__ __launch_bounds__(SK* kWave) void int8_head_mfma_kernel(const int8_t*
   }
   if constexpr (AM) {
     __syncthreads();
-    if (threadIdx.x < m) atomicMax(&keys[threadIdx.x], wg_key[threadIdx.x]);
+    if (threadIdx.x < m) atomicMax(argmax_bin(keys, threadIdx.x), wg_key[threadIdx.x]);
   }
 }
 
@@ -391,16 +406,31 @@ void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, 
   }
 }
 
-__global__ void argmax_init_kernel(unsigned long long* keys, int m) {
-  if (threadIdx.x < m) keys[threadIdx.x] = 0ull;
-}
-
-__global__ void argmax_finish_kernel(const unsigned long long* __restrict__ keys, int m, int32_t* __restrict__ token,
-                                     float* __restrict__ logit) {
-  if (threadIdx.x < m) {
-    const unsigned long long key = keys[threadIdx.x];
-    token[threadIdx.x] = argmax_key_row(key);
-    if (logit) logit[threadIdx.x] = argmax_key_logit(key);
+// One wave per activation row: the row's bins are read (four per lane), the
+// maximum is reduced across the wave, and the bins are set back to zero so
+// that the workspace is ready for the next call without a clearing launch.
+__global__ __launch_bounds__(8 * kWave) void argmax_finish_kernel(unsigned long long* __restrict__ keys, int m,
+                                                                  int32_t* __restrict__ token,
+                                                                  float* __restrict__ logit) {
+  static_assert(kArgmaxBins % kWave == 0, "whole bins per lane");
+  const int row = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (row >= m) return;  // whole waves leave together
+  unsigned long long key = 0ull;
+#pragma unroll
+  for (int b = lane; b < kArgmaxBins; b += kWave) {
+    unsigned long long* p = keys + (static_cast<int64_t>(row) * kArgmaxBins + b) * kArgmaxStride;
+    const unsigned long long v = *p;
+    key = v > key ? v : key;
+    *p = 0ull;
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off /= 2) {
+    const unsigned long long o = __shfl_xor(key, off, kWave);
+    key = o > key ? o : key;
+  }
+  if (lane == 0) {
+    token[row] = argmax_key_row(key);
+    if (logit) logit[row] = argmax_key_logit(key);
   }
 }
 
@@ -430,10 +460,9 @@ hipError_t launch_int8_head(const int8_t* w, const float* scale, int64_t n, int6
 
 hipError_t launch_int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
                                    unsigned long long* keys, int32_t* token, float* logit, hipStream_t stream) {
-  hipLaunchKernelGGL(argmax_init_kernel, dim3(1), dim3(kWave), 0, stream, keys, m);
   const hipError_t e = dispatch_head<true>(w, scale, n, k, x, m, nullptr, keys, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_finish_kernel, dim3(1), dim3(kWave), 0, stream, keys, m, token, logit);
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(1), dim3(8 * kWave), 0, stream, keys, m, token, logit);
   return hipGetLastError();
 }
 

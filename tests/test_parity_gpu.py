@@ -396,6 +396,44 @@ def test_head_argmax_full_size(pbg, m):
         assert abs(float(logit.cpu().numpy()[i]) - ref[i, i]) <= b[i, i]
 
 
+def test_head_argmax_workspace_reuse_and_graph(pbg):
+    """One workspace across calls with different m: every call leaves it zero, results match the
+    plain head; a captured call replayed on new activations matches eager calls."""
+    n, k = 40000, 4096
+    say("argmax workspace reuse")
+    w = synth.head_weights_device(synth.SEED_HEAD + 1, n, k, "cuda:0")
+    s = synth.row_scales_device(synth.SEED_HEAD + 1, n, "cuda:0")
+    keys = torch.zeros(8 * pbg.binding.ARGMAX_KEYS_PER_ROW, dtype=torch.int64, device="cuda:0")
+    for m in (8, 1, 3, 8, 2):
+        x = dev(synth.activations(500 + m, m, k))
+        tok, logit = pbg.int8_head_argmax(w, s, x, keys=keys)
+        y = pbg.int8_head_gemv(w, s, x)
+        assert torch.equal(tok.long(), torch.argmax(y, dim=1))
+        assert torch.equal(logit, y.gather(1, tok.long()[:, None])[:, 0])
+        assert int(torch.count_nonzero(keys)) == 0
+    m = 7
+    xb = dev(synth.activations(600, m, k))
+    tok_b = torch.empty(m, dtype=torch.int32, device="cuda:0")
+    lg_b = torch.empty(m, dtype=torch.float32, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pbg.int8_head_argmax(w, s, xb, keys, tok_b, lg_b)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pbg.int8_head_argmax(w, s, xb, keys, tok_b, lg_b)
+    eager_keys = torch.zeros_like(keys)
+    for rep in range(4):
+        xb.copy_(dev(synth.activations(601 + rep, m, k)))
+        graph.replay()
+        torch.cuda.synchronize()
+        tok_e, lg_e = pbg.int8_head_argmax(w, s, xb, keys=eager_keys)
+        torch.cuda.synchronize()
+        assert torch.equal(tok_b, tok_e) and torch.equal(lg_b, lg_e), rep
+        assert int(torch.count_nonzero(keys)) == 0
+
+
 def test_embedding_gather_exact(pbg):
     n, k = 777, 4100
     table = synth.int8_full_range(20000, n, k)
