@@ -61,28 +61,28 @@ __device__ __forceinline__ void pair_ops(uint64_t w, uint32_t& op0, uint32_t& op
   }
 }
 
+// Step T of a chunk: operand T of each of the four words into its own
+// accumulator, then step T + 1. Each step's operands die at once, so only a
+// few decode registers are live at any time.
 template <int T>
-__device__ __forceinline__ void chunk_ops(uint64_t lo, uint64_t hi, uint32_t (&op)[4][8]) {
-  pair_ops<T>(lo, op[0][T], op[1][T]);
-  pair_ops<T>(hi, op[2][T], op[3][T]);
-  if constexpr (T < 7) chunk_ops<T + 1>(lo, hi, op);
+__device__ __forceinline__ void chunk_steps(uint64_t lo, uint64_t hi, const uint32_t* xp, float (&a)[4]) {
+  uint32_t o0, o1, o2, o3;
+  pair_ops<T>(lo, o0, o1);
+  pair_ops<T>(hi, o2, o3);
+  a[0] = dot2(o0, xp[T], a[0]);
+  a[1] = dot2(o1, xp[8 + T], a[1]);
+  a[2] = dot2(o2, xp[16 + T], a[2]);
+  a[3] = dot2(o3, xp[24 + T], a[3]);
+  if constexpr (T < 7) chunk_steps<T + 1>(lo, hi, xp, a);
 }
 
 // Sum over one 16-byte chunk (4 words, 64 codes) against 32 activation pairs.
 // The four words feed four independent accumulators, interleaved so that a
 // single wave per SIMD still keeps the dot unit busy.
 __device__ __forceinline__ float chunk_dot(const uint4& w, const uint32_t* xp, float acc) {
-  uint32_t op[4][8];
-  chunk_ops<0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, op);
-  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    a0 = dot2(op[0][t], xp[t], a0);
-    a1 = dot2(op[1][t], xp[8 + t], a1);
-    a2 = dot2(op[2][t], xp[16 + t], a2);
-    a3 = dot2(op[3][t], xp[24 + t], a3);
-  }
-  return acc + ((a0 + a1) + (a2 + a3));
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  chunk_steps<0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, xp, a);
+  return acc + ((a[0] + a[1]) + (a[2] + a[3]));
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));

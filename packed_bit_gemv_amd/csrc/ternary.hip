@@ -364,9 +364,9 @@ hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64
   // are non-temporal (each byte is read once per call).
   switch (slices) {
     case 1:
-      if (n >= 8192) launch_gemv_cfg<1, 8, 3, true>(packed, scale, n, k, x, y, stream);
-      else if (n >= 2048) launch_gemv_cfg<1, 8, 1, true>(packed, scale, n, k, x, y, stream);
-      else launch_gemv_cfg<1, 2, 1, true>(packed, scale, n, k, x, y, stream);
+      if (n >= 8192) launch_gemv_cfg<1, 4, 3, true>(packed, scale, n, k, x, y, stream);
+      else if (n >= 2048) launch_gemv_cfg<1, 4, 2, true>(packed, scale, n, k, x, y, stream);
+      else launch_gemv_cfg<1, 4, 1, true>(packed, scale, n, k, x, y, stream);
       break;
     case 2: launch_gemv_cfg<2, 4, 2, true>(packed, scale, n, k, x, y, stream); break;
     case 3: launch_gemv_cfg<3, 4, 2, true>(packed, scale, n, k, x, y, stream); break;
