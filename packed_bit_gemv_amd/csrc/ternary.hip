@@ -5,12 +5,11 @@
 // themselves, introduction; per-row scale, "Where the bytes live"; a drafted run
 // scored in one forward pass, "speculative").
 //
-// Work split (M = 1): a wave owns R consecutive rows and one 4,096-column
-// K-slice of them. Lane l streams 16-byte chunks (64 codes) of each row, keeps
-// the 64 matching activations in registers as fp16 pairs and accumulates fp32
+// Work split (M = 1): a wave owns R consecutive rows (R <= 4) over the whole
+// K. Lane l streams the 16-byte chunks (64 codes) l, l + 64, ... of each row,
+// reads the matching activations from LDS as fp16 pairs and accumulates fp32
 // partial sums with v_dot2; every row load of the wave is in flight before the
-// first decode. Rows are finished four at a time by a transposed cross-lane
-// reduction; K-slices of one row meet in LDS.
+// first decode. The rows are finished by one transposed cross-lane reduction.
 #include "pbg_device.hpp"
 #include "pbg_internal.hpp"
 
@@ -20,36 +19,35 @@ namespace {
 constexpr int kRowsPerWave = 4;  // small-M kernel
 constexpr int kGemvWaves = 4;
 
-// M = 1, fast path: k % 8 == 0, x 16-byte aligned and at most 4 K-slices of
-// 4,096 columns (one per wave of a row group). A workgroup holds G row
-// groups x SW K-slices; wave (g, s) owns R consecutive rows and the 16-byte
-// chunk s*64 + lane of each of them.
-//  1. Every thread loads its share of the workgroup's activations, then a
-//     barrier: all activation loads are queued in the vector memory pipe
-//     before any weight load, so they return first.
-//  2. Each wave issues all R row loads (rows past n clamped to n-1) and the
-//     row scales, unconditionally, so the compiler can retire them one row
-//     at a time.
-//  3. The activations go through LDS (q-major, conflict-free reads) into 32
-//     fp16 pairs per lane, and the rows are decoded as they arrive.
-//  4. Rows are reduced four at a time across the wave; with SW > 1 the
-//     per-slice sums meet in LDS and are added in slice order.
-template <int SW, int G, int R, bool NT = false>
-__global__ __launch_bounds__(SW* G* kWave) void ternary_gemv_kernel(const uint4* __restrict__ packed,
-                                                                     const float* __restrict__ scale, int64_t n,
-                                                                     int64_t k, int64_t chunks,
-                                                                     const uint16_t* x,  // not restrict: keeps
-                                                                     float* __restrict__ y) {  // its loads above the barrier
-  constexpr int kThreads = SW * G * kWave;
-  constexpr int kChunks = SW * kWave;        // 16-byte weight chunks per row in this workgroup
-  constexpr int kGroups = kChunks * 8;       // groups of 8 activations
+// M = 1, fast path: k % 8 == 0, x 16-byte aligned and CPL = ceil(k / 4,096)
+// <= 4 chunks per lane. A workgroup holds G waves; wave g owns R consecutive
+// rows and lane l the chunks l + 64 j (j < CPL) of each of them.
+//  1. Every thread loads its share of the activations, then a barrier: all
+//     activation loads are queued in the vector memory pipe before any weight
+//     load, so they return first.
+//  2. Each wave issues all R * CPL row loads (rows past n and chunks past the
+//     row clamped) and the row scale, unconditionally, so the compiler can
+//     retire them in order.
+//  3. The activations go through LDS, chunk-major and conflict-free; for each
+//     j the lane reads its 32 fp16 pairs once and decodes that chunk of all R
+//     rows, so every activation is read from LDS once per wave.
+//  4. One transposed reduction over the wave finishes the R rows.
+// Splitting K across the waves of a workgroup instead (and adding the slices
+// in LDS) measured 9-25 % slower for CPL = 2..4 on MI355X.
+template <int CPL, int G, int R>
+__global__ __launch_bounds__(G* kWave) void ternary_gemv_kernel(const uint4* __restrict__ packed,
+                                                                const float* __restrict__ scale, int64_t n,
+                                                                int64_t k, int64_t chunks,
+                                                                const uint16_t* x,  // not restrict: keeps its
+                                                                float* __restrict__ y) {  // loads above the barrier
+  static_assert(R >= 1 && R <= 4, "one reduction finishes the rows");
+  constexpr int kThreads = G * kWave;
+  constexpr int kGroups = CPL * kWave * 8;  // 16-byte activation groups of the CPL chunks of every lane
   constexpr int kXPer = (kGroups + kThreads - 1) / kThreads;
-  constexpr int kRed = (R + 3) / 4;
-  __shared__ uint4 xs[kGroups];              // group (c, q) at q * kChunks + c
+  __shared__ uint4 xs[kGroups];             // group q of chunk 64 j + l at (8 j + q) * 64 + l
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int g = wave / SW, s = wave % SW;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * G + g) * R;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * G + wave) * R;
   const int64_t groups = k / 8;
   const uint4* xg = reinterpret_cast<const uint4*>(x);
 
@@ -65,81 +63,49 @@ __global__ __launch_bounds__(SW* G* kWave) void ternary_gemv_kernel(const uint4*
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. rows and scales
-  const int64_t c = static_cast<int64_t>(s) * kWave + lane;
-  const int64_t cc = c < chunks ? c : chunks - 1;
-  uint4 w[R];
+  // 2. rows and scale
+  uint4 w[R][CPL];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const uint4* src = packed + (row0 + i < n ? row0 + i : n - 1) * chunks + cc;
-    w[i] = NT ? load_nt(src) : *src;
+  for (int j = 0; j < CPL; ++j) {
+    const int64_t c = lane + static_cast<int64_t>(kWave) * j;
+    const int64_t cc = c < chunks ? c : chunks - 1;
+#pragma unroll
+    for (int i = 0; i < R; ++i) w[i][j] = load_nt(packed + (row0 + i < n ? row0 + i : n - 1) * chunks + cc);
   }
   const int slot = reduce4_slot(lane);
-  float sc[kRed];
-#pragma unroll
-  for (int q = 0; q < kRed; ++q) {
-    const int64_t r = row0 + 4 * q + (slot < 0 ? 0 : slot);
-    sc[q] = scale[r < n ? r : n - 1];
-  }
+  const int64_t rs = row0 + (slot < 0 ? 0 : slot);
+  const float sc = scale[rs < n ? rs : n - 1];
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. activations through LDS into registers
+  // 3. activations through LDS (zero past k), decoded chunk by chunk
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
     const int gi = threadIdx.x + i * kThreads;
     if (gi < kGroups) {
-      const uint4 v = gi < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);  // zero past k
-      xs[(gi & 7) * kChunks + (gi >> 3)] = v;
+      const int c = gi >> 3, q = gi & 7;
+      xs[((c >> 6) * 8 + q) * kWave + (c & (kWave - 1))] = gi < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
     }
   }
   __syncthreads();
-  uint32_t xp[32];
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint4 v = xs[q * kChunks + s * kWave + lane];
-    xp[4 * q + 0] = v.x;
-    xp[4 * q + 1] = v.y;
-    xp[4 * q + 2] = v.z;
-    xp[4 * q + 3] = v.w;
+  for (int j = 0; j < CPL; ++j) {
+    uint32_t xp[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = xs[(j * 8 + q) * kWave + lane];
+      xp[4 * q + 0] = v.x;
+      xp[4 * q + 1] = v.y;
+      xp[4 * q + 2] = v.z;
+      xp[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) acc[i] = chunk_dot(w[i][j], xp, acc[i]);
   }
-  float acc[4 * kRed];
-#pragma unroll
-  for (int i = 0; i < 4 * kRed; ++i) acc[i] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < R; ++i) acc[i] = chunk_dot(w[i], xp, 0.0f);
 
   // 4. reduction and epilogue
-  float red[kRed];
-#pragma unroll
-  for (int q = 0; q < kRed; ++q) red[q] = wave_reduce4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-  if constexpr (SW == 1) {
-    if (slot >= 0) {
-#pragma unroll
-      for (int q = 0; q < kRed; ++q) {
-        const int64_t r = row0 + 4 * q + slot;
-        if (4 * q + slot < R && r < n) y[r] = red[q] * (sc[q] * kCodeUnitInv);
-      }
-    }
-  } else {
-    __shared__ float part[G][SW][4 * kRed];
-    if (slot >= 0) {
-#pragma unroll
-      for (int q = 0; q < kRed; ++q) part[g][s][4 * q + slot] = red[q] * kCodeUnitInv;
-    }
-    __syncthreads();
-    if (s == 0 && slot >= 0) {
-#pragma unroll
-      for (int q = 0; q < kRed; ++q) {
-        const int64_t r = row0 + 4 * q + slot;
-        if (4 * q + slot < R && r < n) {
-          float sum = part[g][0][4 * q + slot];
-#pragma unroll
-          for (int t = 1; t < SW; ++t) sum += part[g][t][4 * q + slot];
-          y[r] = sum * sc[q];
-        }
-      }
-    }
-  }
+  const float red = wave_reduce4(acc[0], acc[1], acc[2], acc[3]);
+  if (slot >= 0 && slot < R && row0 + slot < n) y[row0 + slot] = red * (sc * kCodeUnitInv);
 }
 
 // M = 1, any k and any 2-byte-aligned x: a wave owns 4 rows, loads are
@@ -168,12 +134,12 @@ __global__ __launch_bounds__(4 * kWave) void ternary_gemv_generic_kernel(const u
   if (slot >= 0 && row0 + slot < n) y[row0 + slot] = r * (scale[row0 + slot] * kCodeUnitInv);
 }
 
-template <int SW, int G, int R, bool NT = false>
+template <int CPL, int G, int R>
 void launch_gemv_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
                      hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(G) * R;
   const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL((ternary_gemv_kernel<SW, G, R, NT>), grid, dim3(SW * G * kWave), 0, stream,
+  hipLaunchKernelGGL((ternary_gemv_kernel<CPL, G, R>), grid, dim3(G * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
 }
 
@@ -359,18 +325,28 @@ hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64
                        reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
     return hipGetLastError();
   }
-  // Launch shapes measured on MI355X (rotating weight pools): about 3-4 waves
-  // of few rows per SIMD, so that several waves decode at once; weight loads
-  // are non-temporal (each byte is read once per call).
+  // Launch shapes from graph-timed sweeps on MI355X (rotating weight pools
+  // larger than the Infinity Cache); weight loads are non-temporal (each byte
+  // is read once per call).
+  const bool big = n >= 2048;
   switch (slices) {
     case 1:
-      if (n >= 8192) launch_gemv_cfg<1, 4, 3, true>(packed, scale, n, k, x, y, stream);
-      else if (n >= 2048) launch_gemv_cfg<1, 4, 2, true>(packed, scale, n, k, x, y, stream);
-      else launch_gemv_cfg<1, 4, 1, true>(packed, scale, n, k, x, y, stream);
+      if (n >= 8192) launch_gemv_cfg<1, 4, 3>(packed, scale, n, k, x, y, stream);
+      else if (big) launch_gemv_cfg<1, 4, 2>(packed, scale, n, k, x, y, stream);
+      else launch_gemv_cfg<1, 4, 1>(packed, scale, n, k, x, y, stream);
       break;
-    case 2: launch_gemv_cfg<2, 4, 2, true>(packed, scale, n, k, x, y, stream); break;
-    case 3: launch_gemv_cfg<3, 4, 2, true>(packed, scale, n, k, x, y, stream); break;
-    default: launch_gemv_cfg<4, 4, 1, true>(packed, scale, n, k, x, y, stream); break;
+    case 2:
+      if (big) launch_gemv_cfg<2, 4, 2>(packed, scale, n, k, x, y, stream);
+      else launch_gemv_cfg<2, 4, 1>(packed, scale, n, k, x, y, stream);
+      break;
+    case 3:
+      if (big) launch_gemv_cfg<3, 8, 1>(packed, scale, n, k, x, y, stream);
+      else launch_gemv_cfg<3, 4, 1>(packed, scale, n, k, x, y, stream);
+      break;
+    default:
+      if (big) launch_gemv_cfg<4, 8, 1>(packed, scale, n, k, x, y, stream);
+      else launch_gemv_cfg<4, 4, 1>(packed, scale, n, k, x, y, stream);
+      break;
   }
   return hipGetLastError();
 }

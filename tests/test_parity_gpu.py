@@ -120,6 +120,21 @@ def test_gemv_exact_probe(pbg, n, k):
     assert np.array_equal(y, ref)
 
 
+# one shape per M = 1 launch configuration (chunks per lane 1..4, small and large n),
+# several with a partial last chunk
+@pytest.mark.parametrize("n,k", [(9000, 4096), (2100, 4096), (700, 4040), (2100, 8192), (1500, 8000),
+                                 (2049, 12296), (333, 12288), (2050, 16000), (300, 16384)])
+def test_gemv_launch_shapes_exact(pbg, n, k):
+    say(f"gemv launch shape n={n} k={k}")
+    codes = synth.ternary_codes(2500 + n + k, n, k)
+    x = synth.probe_activations(3500 + k, 1, k)[0]
+    s = synth.pow2_scales(4500 + n, n)
+    ref = oracle.ternary_gemv(oracle.pack(codes)[0], s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    y = pbg.ternary_gemv(p, dev(s), k, dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, ref)
+
+
 @pytest.mark.parametrize("n,k", SHAPES_SMALL)
 def test_gemv_random_tolerance(pbg, n, k):
     say(f"gemv random n={n} k={k}")
