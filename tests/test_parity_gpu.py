@@ -472,3 +472,79 @@ def test_embedding_gather_full_table(pbg):
     sub = table[rows].cpu().numpy()
     ref = oracle.embedding_gather(sub, s.cpu().numpy()[tokens], np.arange(len(tokens)))
     assert np.array_equal(out, ref)
+
+
+# --------------------------------------------------------------------------
+# Maximum sizes (PBG_MAX_K, PBG_MAX_N): the largest row and the largest grids
+# --------------------------------------------------------------------------
+def test_gemv_max_k(pbg):
+    """k = 2^24 (one row per 4 MiB, the element-guarded kernel): exact probe with 99 % zeros,
+    so every fp32 partial sum stays an exact integer."""
+    n, k = 3, 1 << 24
+    say(f"gemv max k n={n} k={k}")
+    codes = synth.ternary_codes(31, n, k, synth.balanced(0.99))
+    x = synth.probe_activations(32, 1, k)[0]
+    s = synth.pow2_scales(33, n)
+    ref_p = oracle.pack(codes)[0]
+    ref = oracle.ternary_gemv(ref_p, s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    assert np.array_equal(host_words(p), ref_p)
+    y = pbg.ternary_gemv(p, dev(s), k, dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, ref)
+
+
+def test_gemv_and_head_max_n(pbg):
+    """n = 2^24 rows (the largest grids of the M = 1 GEMV and of the head): sampled rows, the last
+    rows included, against the oracle; exact probes."""
+    n, k = 1 << 24, 16
+    say(f"gemv/head max n n={n} k={k}")
+    codes = synth.ternary_codes_device(34, n, k, synth.GLOBAL_DIST, "cuda:0")
+    x = synth.probe_activations(35, 1, k)[0]
+    s_host = synth.pow2_scales(36, 4096)
+    s = dev(np.resize(s_host, n))  # scales repeat every 4,096 rows
+    p, _, st = pbg.pack_ternary(codes)
+    y = pbg.ternary_gemv(p, s, k, dev(x)).cpu().numpy().astype(np.float64)
+    rng = np.random.Generator(np.random.PCG64(37))
+    rows = np.unique(np.concatenate([rng.choice(n, size=4096, replace=False), np.arange(n - 16, n)]))
+    idx = torch.from_numpy(rows).to("cuda:0")
+    c_rows = codes[idx].cpu().numpy()
+    s_rows = s_host[rows % 4096]
+    ref = oracle.ternary_gemv(oracle.pack(c_rows)[0], s_rows, k, x)
+    assert np.array_equal(y[rows], ref)
+    assert int(st.cpu()[0] + st.cpu()[1] + st.cpu()[2]) == n * k
+    del p, y
+    # the int8 head at the same row count
+    w = synth.head_weights_device(38, n, k, "cuda:0")
+    yh = pbg.int8_head_gemv(w, s, dev(x[None, :])).cpu().numpy()[0].astype(np.float64)
+    w_rows = w[idx].cpu().numpy()
+    href = oracle.int8_head_gemv(w_rows, s_rows, x[None, :])[0]
+    assert np.array_equal(yh[rows], href)
+
+
+def test_ffn_max_d_ff(pbg):
+    """d_ff = 2^24 with d_model = 8 (the largest gate/up grid; down is one 16M-column row group):
+    integer probe, h and y exact."""
+    d_model, d_ff = 8, 1 << 24
+    say(f"ffn max d_ff d_model={d_model} d_ff={d_ff}")
+    x = np.array([1, -1, 1, 1, -1, 1, -1, -1], dtype=np.float16)
+    sx = np.where(x > 0, 1, -1).astype(np.int8)
+    # gate rows: sign(x) in every column (negated on rows r = 3 mod 5) and scale 8, so g = +-64;
+    # up rows: one code sign(x_j) at column j = r % 8, so u = 1
+    gate = np.broadcast_to(sx, (5, d_model)).copy()
+    gate[3] = -sx
+    g_codes = torch.from_numpy(gate).to("cuda:0").repeat((d_ff + 4) // 5, 1)[:d_ff].contiguous()
+    u_codes = torch.zeros((d_ff, d_model), dtype=torch.int8, device="cuda:0")
+    cols = torch.arange(d_ff, device="cuda:0") % d_model
+    u_codes[torch.arange(d_ff, device="cuda:0"), cols] = torch.from_numpy(sx).to("cuda:0")[cols]
+    gs = torch.full((d_ff,), 8.0, dtype=torch.float32, device="cuda:0")
+    us = torch.ones(d_ff, dtype=torch.float32, device="cuda:0")
+    down = synth.ternary_codes(39, d_model, d_ff, synth.balanced(0.999))
+    sd = synth.pow2_scales(40, d_model)
+    keep = np.arange(d_ff) % 5 != 3
+    h_exp = np.where(keep, 64.0, 0.0)  # silu(64) * 1 = 64 exactly; silu(-64) * 1 rounds to 0 in fp16
+    assert np.all(np.count_nonzero(down, axis=1) * 64 < 2 ** 24)  # every partial sum an exact fp32 integer
+    y_exp = 64.0 * down[:, keep].sum(axis=1, dtype=np.int64).astype(np.float64) * sd.astype(np.float64)
+    h, y = pbg.ternary_ffn_swiglu(pbg.pack_ternary(g_codes)[0], gs, pbg.pack_ternary(u_codes)[0], us,
+                                  gpu_pack(pbg, down)[0], dev(sd), dev(x))
+    assert np.array_equal(h.cpu().numpy().astype(np.float64), h_exp)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_exp)
