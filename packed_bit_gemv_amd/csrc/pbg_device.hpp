@@ -85,6 +85,34 @@ __device__ __forceinline__ float chunk_dot(const uint4& w, const uint32_t* xp, f
   return acc + ((a[0] + a[1]) + (a[2] + a[3]));
 }
 
+// M activation rows at once: operand t of the four words is decoded once and
+// feeds one dot2 per activation row (xp[m] holds row m's 32 pairs).
+template <int M, int T>
+__device__ __forceinline__ void chunk_steps_m(uint64_t lo, uint64_t hi, const uint32_t (*xp)[32], float (&a)[M][4]) {
+  uint32_t o0, o1, o2, o3;
+  pair_ops<T>(lo, o0, o1);
+  pair_ops<T>(hi, o2, o3);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    a[m][0] = dot2(o0, xp[m][T], a[m][0]);
+    a[m][1] = dot2(o1, xp[m][8 + T], a[m][1]);
+    a[m][2] = dot2(o2, xp[m][16 + T], a[m][2]);
+    a[m][3] = dot2(o3, xp[m][24 + T], a[m][3]);
+  }
+  if constexpr (T < 7) chunk_steps_m<M, T + 1>(lo, hi, xp, a);
+}
+
+// acc[m] += the chunk's sum against activation row m.
+template <int M>
+__device__ __forceinline__ void chunk_dot_m(const uint4& w, const uint32_t (*xp)[32], float* acc) {
+  float a[M][4];
+#pragma unroll
+  for (int m = 0; m < M; ++m) a[m][0] = a[m][1] = a[m][2] = a[m][3] = 0.0f;
+  chunk_steps_m<M, 0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, xp, a);
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] += (a[m][0] + a[m][1]) + (a[m][2] + a[m][3]);
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte load marked non-temporal (streamed once, not kept in the caches).

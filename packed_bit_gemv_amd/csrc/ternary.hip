@@ -108,6 +108,101 @@ __global__ __launch_bounds__(G* kWave) void ternary_gemv_kernel(const uint4* __r
   if (slot >= 0 && slot < R && row0 + slot < n) y[row0 + slot] = red * (sc * kCodeUnitInv);
 }
 
+// 2 <= M <= 3, fast path (same conditions as the M = 1 fast path, K <= 12,288):
+// the M = 1 kernel with M activation rows. All M rows go through LDS; for
+// each chunk the lane reads the 32 fp16 pairs of every row once, decodes
+// each operand once and feeds it to M dot2s, so the decode is shared and the
+// weights are read once for all M rows. The R * M sums are reduced four at a
+// time. Past M = 3 the activation pairs no longer fit in registers and the
+// matrix-core kernel below takes over.
+template <int CPL, int G, int R, int M>
+__global__ __launch_bounds__(G* kWave) void ternary_gemm_rows_kernel(const uint4* __restrict__ packed,
+                                                                     const float* __restrict__ scale, int64_t n,
+                                                                     int64_t k, int64_t chunks, const uint16_t* x,
+                                                                     float* __restrict__ y) {
+  constexpr int kThreads = G * kWave;
+  constexpr int kGroups = CPL * kWave * 8;  // 16-byte activation groups per activation row
+  constexpr int kXPer = (M * kGroups + kThreads - 1) / kThreads;
+  constexpr int kVals = R * M;              // sum (row i, activation row m) at i * M + m
+  constexpr int kRed = (kVals + 3) / 4;
+  __shared__ uint4 xs[M][kGroups];          // group q of chunk 64 j + l at (8 j + q) * 64 + l
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * G + wave) * R;
+  const int64_t groups = k / 8;
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+
+  uint4 xv[kXPer];
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int gi = threadIdx.x + i * kThreads;
+    const int m = gi / kGroups, g = gi % kGroups;
+    xv[i] = xg[m < M && g < groups ? m * groups + g : 0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");  // activation loads queue ahead of the weight loads
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint4 w[R][CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int64_t c = lane + static_cast<int64_t>(kWave) * j;
+    const int64_t cc = c < chunks ? c : chunks - 1;
+#pragma unroll
+    for (int i = 0; i < R; ++i) w[i][j] = load_nt(packed + (row0 + i < n ? row0 + i : n - 1) * chunks + cc);
+  }
+  const int slot = reduce4_slot(lane);
+  float sc[kRed];
+#pragma unroll
+  for (int q = 0; q < kRed; ++q) {
+    const int idx = 4 * q + (slot < 0 ? 0 : slot);
+    const int64_t r = row0 + (idx < kVals ? idx / M : 0);
+    sc[q] = scale[r < n ? r : n - 1];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int gi = threadIdx.x + i * kThreads;
+    const int m = gi / kGroups, g = gi % kGroups;
+    if (m < M) {
+      const int c = g >> 3, q = g & 7;
+      xs[m][((c >> 6) * 8 + q) * kWave + (c & (kWave - 1))] = g < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();
+  float acc[4 * kRed];
+#pragma unroll
+  for (int i = 0; i < 4 * kRed; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    uint32_t xp[M][32];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 v = xs[m][(j * 8 + q) * kWave + lane];
+        xp[m][4 * q + 0] = v.x;
+        xp[m][4 * q + 1] = v.y;
+        xp[m][4 * q + 2] = v.z;
+        xp[m][4 * q + 3] = v.w;
+      }
+#pragma unroll
+    for (int i = 0; i < R; ++i) chunk_dot_m<M>(w[i][j], xp, &acc[i * M]);
+  }
+  float red[kRed];
+#pragma unroll
+  for (int q = 0; q < kRed; ++q) red[q] = wave_reduce4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  if (slot >= 0) {
+#pragma unroll
+    for (int q = 0; q < kRed; ++q) {
+      const int idx = 4 * q + slot;
+      const int64_t r = row0 + idx / M;
+      if (idx < kVals && r < n) y[static_cast<int64_t>(idx % M) * n + r] = red[q] * (sc[q] * kCodeUnitInv);
+    }
+  }
+}
+
 // M = 1, any k and any 2-byte-aligned x: a wave owns 4 rows, loads are
 // guarded element by element. Used only when the fast path's layout
 // conditions do not hold.
@@ -296,6 +391,15 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
   }
 }
 
+template <int CPL, int G, int R, int M>
+void launch_rows_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                     hipStream_t stream) {
+  const int64_t rows_per_block = static_cast<int64_t>(G) * R;
+  const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
+  hipLaunchKernelGGL((ternary_gemm_rows_kernel<CPL, G, R, M>), grid, dim3(G * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
+}
+
 template <int SK, int T, int UPW>
 void launch_mfma_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
                      float* y, hipStream_t stream) {
@@ -354,8 +458,28 @@ hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64
 hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
                                      const uint16_t* x, int m, float* y, hipStream_t stream) {
   if (m == 1) return launch_ternary_gemv(packed, scale, n, k, x, y, stream);
+  const int64_t cpl = (words_per_row(k) / 4 + kWave - 1) / kWave;  // chunks per lane of the M-row kernel
+  const bool fast = k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  // Shared decode on the VALU where it beat the matrix cores in graph-timed
+  // sweeps on MI355X: M = 2 up to 12,288 columns, M = 3 for short K and N.
+  if (fast && m == 2 && cpl <= 3) {
+    if (cpl == 1) {
+      if (n >= 8192) launch_rows_cfg<1, 4, 3, 2>(packed, scale, n, k, x, y, stream);
+      else if (n >= 2048) launch_rows_cfg<1, 8, 1, 2>(packed, scale, n, k, x, y, stream);
+      else launch_rows_cfg<1, 4, 1, 2>(packed, scale, n, k, x, y, stream);
+    } else if (cpl == 2) {
+      launch_rows_cfg<2, 8, 1, 2>(packed, scale, n, k, x, y, stream);
+    } else {
+      launch_rows_cfg<3, 8, 1, 2>(packed, scale, n, k, x, y, stream);
+    }
+    return hipGetLastError();
+  }
+  if (fast && m == 3 && cpl == 1 && n < 2048) {
+    launch_rows_cfg<1, 4, 1, 3>(packed, scale, n, k, x, y, stream);
+    return hipGetLastError();
+  }
   const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
-  if (k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && units <= 48) {
+  if (fast && units <= 48) {
     // Launch shapes from a sweep on MI355X at M = 4 and 8: more tiles per
     // workgroup (each activation column reused by more rows) beat more waves.
     if (units <= 16) {
