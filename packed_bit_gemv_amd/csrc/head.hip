@@ -6,6 +6,8 @@
 // turned into the fp16 value b exactly: the byte, biased to b + 128, becomes
 // the low mantissa byte of fp16 0x64xx = 1024 + (b + 128), and one packed fp16
 // subtraction of 1152 leaves b. v_dot2 then accumulates w * x in fp32.
+#include <atomic>
+
 #include "packed_bit_gemv.h"
 #include "pbg_device.hpp"
 #include "pbg_internal.hpp"
@@ -385,6 +387,162 @@ void launch_head_mfma(const int8_t* w, const float* scale, int64_t n, int64_t k,
                      y, keys);
 }
 
+
+// 2 <= M <= 8 with k % 1024 == 0 and k <= 4096 (w and x 16-byte aligned).
+// Persistent: workgroup b converts row blocks b, b + grid, ... of kPTiles
+// 16-row tiles, and x is copied into LDS once per workgroup, by direct
+// global-to-LDS loads, in the order the MFMA B operand reads it: group q
+// (columns 8q .. 8q + 7) of row j sits at ((2 (q / 8) + q % 2) * 4 +
+// (q % 8) / 2) * M + j. Wave (tg, kq) owns tile tg and the contiguous K
+// quarter kq of every row block, kPBatch 64-column units per batch, with the
+// next batch (of this or the next row block) in flight while one is
+// converted. The kPQuarters partial tiles meet in LDS, in a buffer that
+// alternates between row blocks so that one barrier per block suffices.
+constexpr int kPTiles = 2;     // 16-row tiles per row block
+constexpr int kPQuarters = 4;  // K parts per tile
+constexpr int kPBatch = 4;     // 64-column units per batch
+constexpr int kPMaxK = 4096;
+constexpr int kPWaves = kPTiles * kPQuarters;
+constexpr int kPKStep = 64 * kPQuarters * kPBatch;  // k must be a multiple
+
+__device__ __forceinline__ void load_lds16(const uint4* g, uint4* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);  // lane l writes lds_base[l]
+}
+
+template <int M, bool AM>
+__global__ __launch_bounds__(kPWaves* kWave) void int8_head_persist_kernel(const int8_t* __restrict__ w,
+                                                                           const float* __restrict__ scale, int64_t n,
+                                                                           int64_t k, const uint16_t* __restrict__ x,
+                                                                           float* __restrict__ y,
+                                                                           unsigned long long* __restrict__ keys) {
+  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+  typedef float float4_t __attribute__((ext_vector_type(4)));
+  constexpr int kThreads = kPWaves * kWave;
+  constexpr int kRows = kPTiles * 16;
+  static_assert(kRows * M <= kThreads, "one output per thread per row block");
+  __shared__ uint4 xs[M * (kPMaxK / 8)];
+  __shared__ float part[2][kPTiles][kPQuarters][16][M];
+  __shared__ unsigned long long wg_key[AM ? M : 1];
+  if constexpr (AM) {
+    if (threadIdx.x < M) wg_key[threadIdx.x] = 0ull;  // ordered before use by the barrier below
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int tg = wave / kPQuarters, kq = wave % kPQuarters;
+  const int li = lane & 15, lg = lane >> 4;
+  const int groups = static_cast<int>(k / 8);
+  const int64_t chunks = k / 16;
+  const int upw = static_cast<int>(k / (64 * kPQuarters));  // units per wave and row block
+  const int nb = upw / kPBatch;                              // batches per row block
+  const int64_t nrb = (n + kRows - 1) / kRows;
+  const int my_rb = static_cast<int>((nrb - blockIdx.x + gridDim.x - 1) / gridDim.x);
+  const int total = my_rb * nb;
+  const uint4* wq = reinterpret_cast<const uint4*>(w);
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+  const int o = threadIdx.x;  // output (row o / M, column o % M) of each row block
+  auto out_row = [&](int i) { return (blockIdx.x + static_cast<int64_t>(i) * gridDim.x) * kRows + o / M; };
+
+  auto load_batch = [&](int g, uint4 (&wv)[kPBatch]) {
+    const int64_t r = (blockIdx.x + static_cast<int64_t>(g / nb) * gridDim.x) * kRows + tg * 16 + li;
+    const uint4* row = wq + (r < n ? r : n - 1) * chunks;
+    const int u0 = kq * upw + (g % nb) * kPBatch;
+#pragma unroll
+    for (int c = 0; c < kPBatch; ++c) wv[c] = row[4 * (u0 + c) + lg];
+  };
+  uint4 wv[2][kPBatch];
+  if (total > 0) load_batch(0, wv[0]);
+  if (total > 1) load_batch(1, wv[1]);
+  const int64_t r0 = out_row(0);
+  float sc = scale[r0 < n ? r0 : n - 1];  // scale of the next row block's output
+  const int slots = M * groups;
+  for (int base = wave * kWave; base < slots; base += kThreads) {
+    const int s = base + lane;
+    const int j = s % M, t2 = s / M, g = t2 & 3, st = t2 >> 2;
+    if (s < slots) load_lds16(xg + static_cast<int64_t>(j) * groups + 8 * (st >> 1) + 2 * g + (st & 1), &xs[base]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  float4_t d = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto convert = [&](int g, const uint4 (&wb)[kPBatch]) {
+    const int u0 = kq * upw + (g % nb) * kPBatch;
+#pragma unroll
+    for (int c = 0; c < kPBatch; ++c) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        uint4 bx = make_uint4(0u, 0u, 0u, 0u);
+        if (li < M) bx = xs[((2 * (u0 + c) + v) * 4 + lg) * M + li];
+        uint4 ap;
+        int8x4_to_half2x2(v == 0 ? wb[c].x : wb[c].z, ap.x, ap.y);
+        int8x4_to_half2x2(v == 0 ? wb[c].y : wb[c].w, ap.z, ap.w);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), __builtin_bit_cast(half8_t, bx), d,
+                                                   0, 0, 0);
+      }
+    }
+  };
+  auto finish = [&](int g) {  // after the last batch of row block g / nb
+    const int i = g / nb, p = i & 1;
+    if (li < M) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[p][tg][kq][4 * lg + r][li] = d[r];  // rows 4 lg + r of column li
+    }
+    d = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    __syncthreads();
+    const int64_t r = out_row(i);
+    if (o < kRows * M && r < n) {
+      const int lr = o / M, ocol = o % M;
+      float sum = part[p][lr / 16][0][lr % 16][ocol];
+#pragma unroll
+      for (int q = 1; q < kPQuarters; ++q) sum += part[p][lr / 16][q][lr % 16][ocol];
+      const float v = sum * sc;
+      if constexpr (AM) atomicMax(&wg_key[ocol], argmax_key(v, r));
+      else y[static_cast<int64_t>(ocol) * n + r] = v;
+    }
+    const int64_t rn = out_row(i + 1);
+    sc = scale[rn < n ? rn : n - 1];
+  };
+  for (int g = 0; g < total; g += 2) {  // total is even or the last pass has one batch
+    convert(g, wv[0]);
+    if (g + 2 < total) load_batch(g + 2, wv[0]);
+    if (g % nb == nb - 1) finish(g);
+    if (g + 1 < total) {
+      convert(g + 1, wv[1]);
+      if (g + 3 < total) load_batch(g + 3, wv[1]);
+      if ((g + 1) % nb == nb - 1) finish(g + 1);
+    }
+  }
+  if constexpr (AM) {
+    __syncthreads();
+    if (threadIdx.x < M) atomicMax(argmax_bin(keys, threadIdx.x), wg_key[threadIdx.x]);
+  }
+}
+
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int M, bool AM>
+void launch_head_persist(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                         unsigned long long* keys, hipStream_t stream) {
+  // resident workgroups per CU: LDS (160 KB on gfx950) for larger M, else 3 (the best of 2..4 in sweeps)
+  constexpr int kLds = 16 * M * (kPMaxK / 8) + 4 * 2 * kPTiles * kPQuarters * 16 * M;
+  constexpr int kPerCu = (160 * 1024) / kLds < 3 ? (160 * 1024) / kLds : 3;
+  const int64_t nrb = (n + kPTiles * 16 - 1) / (kPTiles * 16);
+  const int64_t cap = static_cast<int64_t>(kPerCu) * compute_units();
+  const dim3 grid(static_cast<unsigned>(nrb < cap ? nrb : cap));
+  hipLaunchKernelGGL((int8_head_persist_kernel<M, AM>), grid, dim3(kPWaves * kWave), 0, stream, w, scale, n, k, x,
+                     y, keys);
+}
+
 template <int M, bool AM>
 void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
                      unsigned long long* keys, hipStream_t stream) {
@@ -393,6 +551,8 @@ void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, 
   const int64_t units = (k / 16 + 3) / 4;  // 64-column units
   if (aligned && M == 1) {
     launch_head_fast<1, 4, 2, 8, AM>(w, scale, n, k, x, y, keys, stream);
+  } else if (aligned && k % kPKStep == 0 && k <= kPMaxK) {
+    launch_head_persist<M, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M >= 3 && units <= 8 * 16) {
     // 8 waves split the units of 4 tiles (64 rows); at M = 2 the
     // wave-per-4-rows kernel is faster (measured).

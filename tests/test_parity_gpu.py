@@ -238,7 +238,8 @@ def test_small_m_config_shapes(pbg, m, proj):
 # int8_head_gemv
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("n,k", [(1, 16), (3, 5), (17, 100), (40, 4096), (33, 4112), (9, 12288), (1000, 4096)])
+@pytest.mark.parametrize("n,k", [(1, 16), (3, 5), (17, 100), (40, 4096), (33, 4112), (9, 12288), (1000, 4096),
+                                 (40000, 1024), (4100, 2048), (33, 3072)])
 def test_head_exact_probe(pbg, m, n, k):
     say(f"head exact m={m} n={n} k={k}")
     w = synth.int8_full_range(10000 + n + k, n, k)
@@ -347,7 +348,8 @@ def test_graph_replay_matches_eager(pbg):
 # Greedy argmax through the head, embedding rows
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
-@pytest.mark.parametrize("n,k", [(1, 16), (17, 100), (40, 4096), (33, 4112), (2000, 4096), (9, 12288)])
+@pytest.mark.parametrize("n,k", [(1, 16), (17, 100), (40, 4096), (33, 4112), (2000, 4096), (9, 12288),
+                                 (40000, 1024), (33, 3072)])
 def test_head_argmax_exact_probe(pbg, m, n, k):
     """Integer activations, power-of-two scales, full-range int8: logits are
     exact on both sides, so the token (lowest index on ties) and its logit
