@@ -426,8 +426,8 @@ def main():
             "kernel": "swiglu_gate_up_kernel",
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gate_up_us, 3),
-            "launch_us_note": "HIP events around a replayed graph of 36 consecutive launches over the pool, "
-                              "divided by 36 (inter-launch gaps included)",
+            "launch_us_note": f"HIP events around a replayed graph of {L} consecutive launches over the pool, "
+                              f"divided by {L} (inter-launch gaps included)",
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
         "extra": extra,
