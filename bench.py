@@ -142,15 +142,34 @@ def cpu_baseline(budget_s: float):
         codes = synth.ternary_codes(synth.tensor_seed(1, p), rows, k, synth.code_dist(1, p))
         samples.append((oracle.pack(codes)[0], synth.row_scales(synth.tensor_seed(1, p), rows), k,
                         synth.activations(synth.x_seed(0), 1, k)[0], rows))
-    done_bytes = 0
-    reps = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        for packed, s, k, x, r in samples:
-            oracle.ternary_gemv(packed, s, k, x)
-            done_bytes += ternary_bytes(r, k)
-        reps += 1
-    dt = time.perf_counter() - t0
+
+    def run(seconds, fn):
+        done, reps, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for packed, s, k, x, r in samples:
+                fn(packed, s, k, x)
+                done += ternary_bytes(r, k)
+            reps += 1
+        return done, reps, time.perf_counter() - t0
+
+    done_bytes, reps, dt = run(budget_s, oracle.ternary_gemv)
+    # the unpack alone, and the whole oracle restricted to one BLAS thread
+    _, u_reps, u_dt = run(budget_s / 6, lambda packed, s, k, x: oracle.unpack(packed, k))
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1):
+            b1, _, dt1 = run(budget_s / 3, oracle.ternary_gemv)
+        one = round(b1 / dt1 / 1e9, 4)
+    except Exception:
+        pass
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(done_bytes / dt / 1e9, 4),
         "unit": "GB/s",
@@ -158,6 +177,9 @@ def cpu_baseline(budget_s: float):
         "kind": "oracle",
         "sample": (f"{reps} passes over the first {rows} rows of layer-1 gate, up and down (M=1), "
                    f"{dt:.1f} s; unpack in NumPy (1 thread) + fp64 matvec in BLAS ({threads} threads)"),
+        "unpack_share": round((u_dt / u_reps) / (dt / reps), 3),
+        "value_1_thread": one,
+        "cpu_model": model,
     }
 
 

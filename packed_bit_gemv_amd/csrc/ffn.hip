@@ -25,7 +25,9 @@ namespace {
 constexpr int kPairs = 2;      // row pairs per wave
 constexpr int kFfnWaves = 4;   // waves per workgroup
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z) with the hardware reciprocal (1 ulp): h is rounded to fp16
+// right after, so an IEEE division would only cost instructions.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 template <int R, int G>
 __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
     const int gi = threadIdx.x + i * kThreads;
-    if (gi < kX) buf[(gi & 7) * kWave + (gi >> 3)] = gi < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+    if (gi < kX) buf[(gi & 7) * kWave + (gi >> 3)] = masked(xv[i], gi < groups);
   }
   __syncthreads();
   uint32_t xp[32];

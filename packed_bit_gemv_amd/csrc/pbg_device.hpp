@@ -61,43 +61,43 @@ __device__ __forceinline__ void pair_ops(uint64_t w, uint32_t& op0, uint32_t& op
   }
 }
 
-// Step T of a chunk: operand T of each of the four words into its own
-// accumulator, then step T + 1. Each step's operands die at once, so only a
-// few decode registers are live at any time.
+// Step T of a chunk: operand T of each of the four words, then step T + 1.
+// Each step's operands die at once, so only a few decode registers are live
+// at any time. One accumulator chain: with several waves per SIMD the
+// dependent dot2s cost no issue slots, while split accumulators would cost a
+// zeroing move and a combining add each per chunk.
 template <int T>
-__device__ __forceinline__ void chunk_steps(uint64_t lo, uint64_t hi, const uint32_t* xp, float (&a)[4]) {
+__device__ __forceinline__ void chunk_steps(uint64_t lo, uint64_t hi, const uint32_t* xp, float& a) {
   uint32_t o0, o1, o2, o3;
   pair_ops<T>(lo, o0, o1);
   pair_ops<T>(hi, o2, o3);
-  a[0] = dot2(o0, xp[T], a[0]);
-  a[1] = dot2(o1, xp[8 + T], a[1]);
-  a[2] = dot2(o2, xp[16 + T], a[2]);
-  a[3] = dot2(o3, xp[24 + T], a[3]);
+  a = dot2(o0, xp[T], a);
+  a = dot2(o1, xp[8 + T], a);
+  a = dot2(o2, xp[16 + T], a);
+  a = dot2(o3, xp[24 + T], a);
   if constexpr (T < 7) chunk_steps<T + 1>(lo, hi, xp, a);
 }
 
-// Sum over one 16-byte chunk (4 words, 64 codes) against 32 activation pairs.
-// The four words feed four independent accumulators, interleaved so that a
-// single wave per SIMD still keeps the dot unit busy.
+// acc + the sum over one 16-byte chunk (4 words, 64 codes) against 32
+// activation pairs.
 __device__ __forceinline__ float chunk_dot(const uint4& w, const uint32_t* xp, float acc) {
-  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  chunk_steps<0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, xp, a);
-  return acc + ((a[0] + a[1]) + (a[2] + a[3]));
+  chunk_steps<0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, xp, acc);
+  return acc;
 }
 
 // M activation rows at once: operand t of the four words is decoded once and
 // feeds one dot2 per activation row (xp[m] holds row m's 32 pairs).
 template <int M, int T>
-__device__ __forceinline__ void chunk_steps_m(uint64_t lo, uint64_t hi, const uint32_t (*xp)[32], float (&a)[M][4]) {
+__device__ __forceinline__ void chunk_steps_m(uint64_t lo, uint64_t hi, const uint32_t (*xp)[32], float* a) {
   uint32_t o0, o1, o2, o3;
   pair_ops<T>(lo, o0, o1);
   pair_ops<T>(hi, o2, o3);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    a[m][0] = dot2(o0, xp[m][T], a[m][0]);
-    a[m][1] = dot2(o1, xp[m][8 + T], a[m][1]);
-    a[m][2] = dot2(o2, xp[m][16 + T], a[m][2]);
-    a[m][3] = dot2(o3, xp[m][24 + T], a[m][3]);
+    a[m] = dot2(o0, xp[m][T], a[m]);
+    a[m] = dot2(o1, xp[m][8 + T], a[m]);
+    a[m] = dot2(o2, xp[m][16 + T], a[m]);
+    a[m] = dot2(o3, xp[m][24 + T], a[m]);
   }
   if constexpr (T < 7) chunk_steps_m<M, T + 1>(lo, hi, xp, a);
 }
@@ -105,15 +105,16 @@ __device__ __forceinline__ void chunk_steps_m(uint64_t lo, uint64_t hi, const ui
 // acc[m] += the chunk's sum against activation row m.
 template <int M>
 __device__ __forceinline__ void chunk_dot_m(const uint4& w, const uint32_t (*xp)[32], float* acc) {
-  float a[M][4];
-#pragma unroll
-  for (int m = 0; m < M; ++m) a[m][0] = a[m][1] = a[m][2] = a[m][3] = 0.0f;
-  chunk_steps_m<M, 0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, xp, a);
-#pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] += (a[m][0] + a[m][1]) + (a[m][2] + a[m][3]);
+  chunk_steps_m<M, 0>(static_cast<uint64_t>(w.y) << 32 | w.x, static_cast<uint64_t>(w.w) << 32 | w.z, xp, acc);
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// v if keep, else zero, by AND masks (no branch, no register copies).
+__device__ __forceinline__ uint4 masked(const uint4& v, bool keep) {
+  const uint32_t k = keep ? 0xFFFFFFFFu : 0u;
+  return make_uint4(v.x & k, v.y & k, v.z & k, v.w & k);
+}
 
 // 16-byte load marked non-temporal (streamed once, not kept in the caches).
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(G* kWave) void ternary_gemv_kernel(const uint4* __r
     const int gi = threadIdx.x + i * kThreads;
     if (gi < kGroups) {
       const int c = gi >> 3, q = gi & 7;
-      xs[((c >> 6) * 8 + q) * kWave + (c & (kWave - 1))] = gi < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+      xs[((c >> 6) * 8 + q) * kWave + (c & (kWave - 1))] = masked(xv[i], gi < groups);
     }
   }
   __syncthreads();
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(G* kWave) void ternary_gemm_rows_kernel(const uint4
     const int m = gi / kGroups, g = gi % kGroups;
     if (m < M) {
       const int c = g >> 3, q = g & 7;
-      xs[m][((c >> 6) * 8 + q) * kWave + (c & (kWave - 1))] = g < groups ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+      xs[m][((c >> 6) * 8 + q) * kWave + (c & (kWave - 1))] = masked(xv[i], g < groups);
     }
   }
   __syncthreads();

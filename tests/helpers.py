@@ -108,7 +108,7 @@ def ffn_probe(seed: int, d_model: int, d_ff: int):
 def swiglu_h_bound(silu_g: np.ndarray, u: np.ndarray, tg: np.ndarray, tu: np.ndarray) -> np.ndarray:
     """Bound on |h - h_ref| for h = fp16(silu(g) * u) when the kernel's g and u
     are within tg and tu of the exact values: silu has slope at most 1.1, the
-    fp32 exp and divide add at most 1e-6 relative, and two fp16 roundings of
+    fp32 exp and reciprocal add at most 1e-6 relative, and two fp16 roundings of
     values that close differ by at most their distance plus one fp16 ulp."""
     a = 1.1 * tg * (np.abs(u) + tu) + np.abs(silu_g) * tu + 1e-6 * np.abs(silu_g * u)
     mag = np.abs(silu_g * u) + a
