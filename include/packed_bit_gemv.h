@@ -30,7 +30,9 @@
  *
  * Conventions for every entry point:
  *   - all array pointers are DEVICE pointers owned by the caller; the library
- *     never allocates, frees or keeps them, and holds no global state;
+ *     never allocates, frees or keeps them. Its only global state is a
+ *     per-device cache of the compute-unit count (read once, atomically), so
+ *     calls from several threads are safe;
  *   - work is enqueued on the caller's `stream` (0 = the null stream) and
  *     the call returns without waiting, except where stated;
  *   - arguments are validated before any HIP call; on a validation error

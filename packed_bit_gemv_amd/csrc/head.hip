@@ -264,7 +264,8 @@ void launch_head_fast(const int8_t* w, const float* scale, int64_t n, int64_t k,
                      x, y, keys);
 }
 
-// 2 <= M <= 8 on the matrix cores (k % 16 == 0, w and x 16-byte aligned).
+// 2 <= M <= 8 on the matrix cores for k the persistent kernel below does not
+// take (k % 16 == 0, w and x 16-byte aligned).
 // v_mfma_f32_16x16x32_f16 takes a 16-row tile of weights converted to fp16
 // (A) and the M activation rows as B columns (zero past M). A lane with row
 // i = lane % 16 and K-group g = lane / 16 loads 16 weights per 64-column unit
@@ -554,8 +555,8 @@ void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, 
   } else if (aligned && k % kPKStep == 0 && k <= kPMaxK) {
     launch_head_persist<M, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M >= 3 && units <= 8 * 16) {
-    // 8 waves split the units of 4 tiles (64 rows); at M = 2 the
-    // wave-per-4-rows kernel is faster (measured).
+    // Other k: 8 waves split the units of 4 tiles (64 rows); at M = 2 the
+    // wave-per-4-rows kernel is faster there (measured).
     if (units <= 8) launch_head_mfma<8, 4, 1, AM>(w, scale, n, k, x, M, y, keys, stream);
     else if (units <= 16) launch_head_mfma<8, 4, 2, AM>(w, scale, n, k, x, M, y, keys, stream);
     else if (units <= 32) launch_head_mfma<8, 4, 4, AM>(w, scale, n, k, x, M, y, keys, stream);
