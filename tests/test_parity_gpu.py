@@ -550,3 +550,83 @@ def test_ffn_max_d_ff(pbg):
                                   gpu_pack(pbg, down)[0], dev(sd), dev(x))
     assert np.array_equal(h.cpu().numpy().astype(np.float64), h_exp)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), y_exp)
+
+
+# --------------------------------------------------------------------------
+# Concurrency: no hidden shared state between calls
+# --------------------------------------------------------------------------
+def test_concurrent_streams_and_threads_match_sequential(pbg):
+    """Calls on two streams at once, and from two host threads with a stream
+    each, give the same bits as the same calls one after another (every
+    kernel sums in a fixed order, and the argmax workspaces are per caller)."""
+    import threading
+
+    say("concurrent streams")
+    n, k, hn = 12288, 4096, 40000
+    codes = synth.ternary_codes_device(synth.tensor_seed(2, "gate"), n, k, synth.code_dist(2, "gate"), "cuda:0")
+    packed = pbg.pack_ternary(codes)[0]
+    del codes
+    s = synth.row_scales_device(synth.tensor_seed(2, "gate"), n, "cuda:0")
+    hw = synth.head_weights_device(synth.SEED_HEAD + 2, hn, k, "cuda:0")
+    hs = synth.row_scales_device(synth.SEED_HEAD + 2, hn, "cuda:0")
+    x = dev(synth.activations(700, 8, k))
+
+    def work_a():
+        return (pbg.ternary_gemv(packed, s, k, x[0]), pbg.ternary_gemm_small(packed, s, k, x[:4]),
+                pbg.int8_head_gemv(hw, hs, x[:3]))
+
+    def work_b(keys):
+        return (pbg.int8_head_argmax(hw, hs, x[:7], keys=keys), pbg.ternary_gemm_small(packed, s, k, x[:2]),
+                pbg.int8_head_gemv(hw, hs, x[:1]))
+
+    keys_a = torch.zeros(8 * pbg.binding.ARGMAX_KEYS_PER_ROW, dtype=torch.int64, device="cuda:0")
+    keys_b = torch.zeros_like(keys_a)
+    ref_a, ref_b = work_a(), work_b(keys_a)
+    torch.cuda.synchronize()
+
+    def same(got, ref):
+        flat_g = [t for g in got for t in (g if isinstance(g, tuple) else (g,))]
+        flat_r = [t for r in ref for t in (r if isinstance(r, tuple) else (r,))]
+        return all(torch.equal(a, b) for a, b in zip(flat_g, flat_r))
+
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(5):
+        with torch.cuda.stream(sa):
+            oa = work_a()
+        with torch.cuda.stream(sb):
+            ob = work_b(keys_b)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert same(oa, ref_a) and same(ob, ref_b)
+    assert int(torch.count_nonzero(keys_b)) == 0
+
+    say("concurrent threads")
+    results, errors = {}, []
+
+    def thread_body(name, fn):
+        try:
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.default_stream())
+            got = []
+            with torch.cuda.stream(st):
+                for _ in range(5):
+                    got.append(fn())
+            st.synchronize()
+            results[name] = got
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    keys_t = torch.zeros_like(keys_a)
+    threads = [threading.Thread(target=thread_body, args=("a", work_a)),
+               threading.Thread(target=thread_body, args=("b", lambda: work_b(keys_t)))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert all(same(g, ref_a) for g in results["a"]) and all(same(g, ref_b) for g in results["b"])
+    assert int(torch.count_nonzero(keys_t)) == 0
