@@ -417,6 +417,14 @@ def main():
         extra["copy_12.6MB_GBs_read_plus_write"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
         del pool, dst, g
 
+        # per-launch floor of a dependent kernel in a graph: 36 launches of a
+        # one-element kernel, timed like the per-linear figures
+        one = torch.zeros(1, dtype=torch.float32, device=device)
+        g = capture(torch, lambda: [one.add_(1.0) for _ in range(36)])
+        ms = time_graphs(torch, [g], 20, 2) / 36
+        extra["launch_floor_us"] = round(ms * 1e3, 3)
+        del g, one
+
     result = {
         "metric": METRIC,
         "value": round(value, 1),
