@@ -220,6 +220,28 @@ int ternary_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, con
                        const float* up_scale, const uint32_t* down_packed, const float* down_scale, int64_t d_model,
                        int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream);
 
+/*
+ * ternary_swiglu_gate_up_small / ternary_ffn_swiglu_small - the two calls
+ * above for 1 <= m <= PBG_MAX_M activation rows, the shape a speculative
+ * verify step scores (Neutrino-1 8B model page, "speculative" section): every
+ * weight byte is read once for all m rows.
+ *   x     fp16 [m][d_model], 16-byte aligned
+ *   h     out, fp16 [m][d_ff], row i = fp16(silu(g_i) * u_i) with g_i, u_i the
+ *         gate and up outputs of x row i; 16-byte aligned
+ *   y     out (ffn only), fp32 [m][d_model], y_i = down h_i, 4-byte aligned
+ * d_model, d_ff, the packs and scales are as for the m = 1 calls (same limits
+ * and alignment); m = 1 runs exactly the m = 1 kernels. Returns PBG_ERR_SHAPE
+ * for m outside [1, PBG_MAX_M].
+ */
+int ternary_swiglu_gate_up_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                                 const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m,
+                                 uint16_t* h, hipStream_t stream);
+
+int ternary_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                             const float* up_scale, const uint32_t* down_packed, const float* down_scale,
+                             int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m, uint16_t* h, float* y,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,7 @@ from .build import LIB_PATH
 
 PBG_ERR_CODE = -4
 ARGMAX_KEYS_PER_ROW = 4096  # PBG_ARGMAX_KEYS_PER_ROW
+MAX_M = 8  # PBG_MAX_M
 
 _c_int = ctypes.c_int
 _c_i64 = ctypes.c_int64
@@ -35,6 +36,9 @@ _SIGNATURES = {
     "int8_embedding_gather": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "ternary_swiglu_gate_up": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "ternary_ffn_swiglu": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "ternary_swiglu_gate_up_small": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "ternary_ffn_swiglu_small": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp,
+                                          _vp]),
 }
 
 
@@ -246,9 +250,21 @@ def int8_embedding_gather(table: torch.Tensor, scale: torch.Tensor, tokens: torc
     return out
 
 
+def _ffn_rows(x: torch.Tensor, d_model: int) -> int:
+    """0 for x [d_model] (one row), m for x [m, d_model] with 1 <= m <= 8."""
+    if x.dim() == 1 and tuple(x.shape) == (d_model,):
+        return 0
+    if x.dim() == 2 and x.shape[1] == d_model and 1 <= x.shape[0] <= MAX_M:
+        return x.shape[0]
+    raise ValueError(f"x must be [{d_model}] or [m, {d_model}] with 1 <= m <= {MAX_M}")
+
+
 def ternary_swiglu_gate_up(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
                            d_model: int, x: torch.Tensor, h: torch.Tensor | None = None) -> torch.Tensor:
-    """h = fp16(silu(gate x) * up x) in one launch; gate, up packed [d_ff, words_per_row(d_model)]."""
+    """h = fp16(silu(gate x) * up x) in one launch; gate, up packed [d_ff, words_per_row(d_model)].
+
+    x fp16 [d_model] gives h [d_ff]; x [m, d_model] (m <= 8, one weight read for all rows) gives h [m, d_ff].
+    """
     for t, name in ((gate, "gate"), (up, "up")):
         _dev(t, name, torch.int32)
     for t, name in ((gate_scale, "gate_scale"), (up_scale, "up_scale")):
@@ -259,16 +275,22 @@ def ternary_swiglu_gate_up(gate: torch.Tensor, gate_scale: torch.Tensor, up: tor
         raise ValueError(f"gate and up must be [d_ff, {words_per_row(d_model)}]")
     if tuple(gate_scale.shape) != (d_ff,) or tuple(up_scale.shape) != (d_ff,):
         raise ValueError("scales must be [d_ff]")
-    if tuple(x.shape) != (d_model,):
-        raise ValueError(f"x must be [{d_model}]")
+    m = _ffn_rows(x, d_model)
+    h_shape = (d_ff,) if m == 0 else (m, d_ff)
     if h is None:
-        h = torch.empty((d_ff,), dtype=torch.float16, device=gate.device)
+        h = torch.empty(h_shape, dtype=torch.float16, device=gate.device)
     _dev(h, "h", torch.float16)
-    if tuple(h.shape) != (d_ff,):
-        raise ValueError("h must be [d_ff]")
-    rc = lib().ternary_swiglu_gate_up(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
-                                      d_model, d_ff, x.data_ptr(), h.data_ptr(), _stream(gate))
-    _check("ternary_swiglu_gate_up", rc)
+    if tuple(h.shape) != h_shape:
+        raise ValueError(f"h must be {list(h_shape)}")
+    if m == 0:
+        rc = lib().ternary_swiglu_gate_up(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                          d_model, d_ff, x.data_ptr(), h.data_ptr(), _stream(gate))
+        _check("ternary_swiglu_gate_up", rc)
+    else:
+        rc = lib().ternary_swiglu_gate_up_small(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(),
+                                                up_scale.data_ptr(), d_model, d_ff, x.data_ptr(), m, h.data_ptr(),
+                                                _stream(gate))
+        _check("ternary_swiglu_gate_up_small", rc)
     return h
 
 
@@ -278,7 +300,8 @@ def ternary_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.T
     """Gated feed-forward block: h = fp16(silu(gate x) * up x), y = down h.
 
     gate, up: packed [d_ff, words_per_row(d_model)]; down: packed [d_model, words_per_row(d_ff)];
-    x fp16 [d_model]. Returns (h fp16 [d_ff], y fp32 [d_model]).
+    x fp16 [d_model] -> (h fp16 [d_ff], y fp32 [d_model]), or x [m, d_model] with m <= 8 ->
+    (h [m, d_ff], y [m, d_model]), each weight read once for all m rows.
     """
     for t, name in ((gate, "gate"), (up, "up"), (down, "down")):
         _dev(t, name, torch.int32)
@@ -292,19 +315,26 @@ def ternary_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.T
         raise ValueError(f"down must be [d_model, {words_per_row(d_ff)}]")
     if tuple(gate_scale.shape) != (d_ff,) or tuple(up_scale.shape) != (d_ff,) or tuple(down_scale.shape) != (d_model,):
         raise ValueError("scales must be [d_ff], [d_ff], [d_model]")
-    if tuple(x.shape) != (d_model,):
-        raise ValueError(f"x must be [{d_model}]")
+    m = _ffn_rows(x, d_model)
+    h_shape = (d_ff,) if m == 0 else (m, d_ff)
+    y_shape = (d_model,) if m == 0 else (m, d_model)
     dev = gate.device
     if h is None:
-        h = torch.empty((d_ff,), dtype=torch.float16, device=dev)
+        h = torch.empty(h_shape, dtype=torch.float16, device=dev)
     if y is None:
-        y = torch.empty((d_model,), dtype=torch.float32, device=dev)
+        y = torch.empty(y_shape, dtype=torch.float32, device=dev)
     _dev(h, "h", torch.float16)
     _dev(y, "y", torch.float32)
-    if tuple(h.shape) != (d_ff,) or tuple(y.shape) != (d_model,):
-        raise ValueError("h must be [d_ff] and y [d_model]")
-    rc = lib().ternary_ffn_swiglu(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
-                                  down.data_ptr(), down_scale.data_ptr(), d_model, d_ff, x.data_ptr(), h.data_ptr(),
-                                  y.data_ptr(), _stream(gate))
-    _check("ternary_ffn_swiglu", rc)
+    if tuple(h.shape) != h_shape or tuple(y.shape) != y_shape:
+        raise ValueError(f"h must be {list(h_shape)} and y {list(y_shape)}")
+    if m == 0:
+        rc = lib().ternary_ffn_swiglu(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                      down.data_ptr(), down_scale.data_ptr(), d_model, d_ff, x.data_ptr(),
+                                      h.data_ptr(), y.data_ptr(), _stream(gate))
+        _check("ternary_ffn_swiglu", rc)
+    else:
+        rc = lib().ternary_ffn_swiglu_small(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(),
+                                            up_scale.data_ptr(), down.data_ptr(), down_scale.data_ptr(), d_model,
+                                            d_ff, x.data_ptr(), m, h.data_ptr(), y.data_ptr(), _stream(gate))
+        _check("ternary_ffn_swiglu_small", rc)
     return h, y

@@ -125,6 +125,120 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
   }
 }
 
+
+// 2 <= M <= 8 activation rows (d_model % 8 == 0, x 16-byte aligned): the same
+// launch on the matrix cores. A 16-row MFMA tile holds 8 gate rows and the
+// same 8 up rows: lane (i, g) reads gate row p0 + i for i < 8 and up row
+// p0 + i - 8 otherwise, so accumulator lanes g = 0, 1 end with the gate sums
+// of the 8 pairs and g = 2, 3 with their up sums, per activation column j.
+// The rest follows the small-M GEMM (ternary.hip): SK waves split the
+// 256-column units of T tiles, one unit's loads ahead; B lane (g, j) holds
+// x_j at the 8 columns that A lane (i, g) decodes; partial tiles meet in LDS
+// in wave order. The epilogue forms h = fp16(silu(g) * u) per pair and row of
+// x.
+template <int SK, int T, int UPW>
+__global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
+    const uint4* __restrict__ gate, const float* __restrict__ gate_scale, const uint4* __restrict__ up,
+    const float* __restrict__ up_scale, int64_t d_model, int64_t d_ff, int64_t chunks, const uint16_t* __restrict__ x,
+    int m, uint16_t* __restrict__ h) {
+  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+  typedef float float4_t __attribute__((ext_vector_type(4)));
+  constexpr int kPairsWg = 8 * T;  // gate/up row pairs of the workgroup
+  __shared__ float part[SK][16 * T][8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t pair_base = static_cast<int64_t>(blockIdx.x) * kPairsWg;
+  const int64_t groups = d_model / 8;
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+  const uint4* src = li < 8 ? gate : up;
+
+  // outputs (pair, column) o = threadIdx.x + e * SK * 64: pair o / 8, column o % 8
+  constexpr int kOut = (kPairsWg * 8 + SK * kWave - 1) / (SK * kWave);
+  float sg[kOut], su[kOut];
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    int64_t r = pair_base + (o < kPairsWg * 8 ? o >> 3 : 0);
+    r = r < d_ff ? r : d_ff - 1;
+    sg[e] = gate_scale[r];
+    su[e] = up_scale[r];
+  }
+  auto load_unit = [&](int q, uint4 (&xb)[8], uint4 (&wv)[T]) {
+    const int64_t u = s + static_cast<int64_t>(SK) * q;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int64_t gi = 32 * u + 8 * lg + v;
+      const bool ok = li < m && gi < groups;
+      xb[v] = xg[ok ? static_cast<int64_t>(li) * groups + gi : 0];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t r = pair_base + 8 * t + (li & 7);
+      const int64_t c = 4 * u + lg;
+      wv[t] = load_nt(src + (r < d_ff ? r : d_ff - 1) * chunks + (c < chunks ? c : chunks - 1));
+    }
+  };
+
+  float4_t d[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xb[2][8], wv[2][T];
+  load_unit(0, xb[0], wv[0]);
+#pragma unroll
+  for (int q = 0; q < UPW; ++q) {
+    if (q + 1 < UPW) load_unit(q + 1, xb[(q + 1) & 1], wv[(q + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t u = s + static_cast<int64_t>(SK) * q;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int64_t gi = 32 * u + 8 * lg + v;
+      const half8_t b = __builtin_bit_cast(half8_t, masked(xb[q & 1][v], li < m && gi < groups));
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
+        const int hh = v & 1;
+        const uint4 ap = make_uint4(code_pair(wd, 4 * hh + 0), code_pair(wd, 4 * hh + 1), code_pair(wd, 4 * hh + 2),
+                                    code_pair(wd, 4 * hh + 3));
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
+      }
+    }
+  }
+  // partial tiles to LDS: lane (g, j) holds tile rows 4g..4g+3 of column j
+  if (li < 8) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[s][16 * t + 4 * lg + r][li] = d[t][r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    const int p = o >> 3, j = o & 7;
+    const int64_t r = pair_base + p;
+    if (o < kPairsWg * 8 && j < m && r < d_ff) {
+      const int tr = 16 * (p >> 3) + (p & 7);  // gate row of the pair in its tile; up row is tr + 8
+      float g = part[0][tr][j], uu = part[0][tr + 8][j];
+#pragma unroll
+      for (int w = 1; w < SK; ++w) {
+        g += part[w][tr][j];
+        uu += part[w][tr + 8][j];
+      }
+      const float hv = silu(g * (sg[e] * kCodeUnitInv)) * (uu * (su[e] * kCodeUnitInv));
+      h[static_cast<int64_t>(j) * d_ff + r] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
+    }
+  }
+}
+
+template <int SK, int T, int UPW>
+void launch_gate_up_mfma(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
+                         int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((d_ff + 8 * T - 1) / (8 * T)));
+  hipLaunchKernelGGL((swiglu_gate_up_mfma_kernel<SK, T, UPW>), grid, dim3(SK * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(gate), gate_scale, reinterpret_cast<const uint4*>(up), up_scale,
+                     d_model, d_ff, words_per_row(d_model) / 4, x, m, h);
+}
 }  // namespace
 
 hipError_t launch_swiglu_gate_up(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
@@ -144,6 +258,25 @@ hipError_t launch_ffn_swiglu(const uint32_t* gate, const float* gate_scale, cons
   const hipError_t e = launch_swiglu_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
   if (e != hipSuccess) return e;
   return launch_ternary_gemv(down, down_scale, d_model, d_ff, h, y, stream);
+}
+
+hipError_t launch_swiglu_gate_up_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                       const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x,
+                                       int m, uint16_t* h, hipStream_t stream) {
+  if (m == 1) return launch_swiglu_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
+  // d_model <= 4,096: at most 16 units of 256 columns, four per wave
+  if (d_ff >= 8192) launch_gate_up_mfma<4, 4, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  else launch_gate_up_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_swiglu_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                   const float* up_scale, const uint32_t* down, const float* down_scale,
+                                   int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* y,
+                                   hipStream_t stream) {
+  const hipError_t e = launch_swiglu_gate_up_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  if (e != hipSuccess) return e;
+  return launch_ternary_gemm_small(down, down_scale, d_model, d_ff, h, m, y, stream);
 }
 
 }  // namespace pbg

@@ -32,6 +32,16 @@ hipError_t launch_ffn_swiglu(const uint32_t* gate, const float* gate_scale, cons
                              const float* up_scale, const uint32_t* down, const float* down_scale, int64_t d_model,
                              int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream);
 
+// The same two for 1 <= m <= 8 activation rows: x [m][d_model], h [m][d_ff], y [m][d_model].
+hipError_t launch_swiglu_gate_up_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                       const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x,
+                                       int m, uint16_t* h, hipStream_t stream);
+
+hipError_t launch_ffn_swiglu_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                   const float* up_scale, const uint32_t* down, const float* down_scale,
+                                   int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* y,
+                                   hipStream_t stream);
+
 // Workgroups one embedding gather launches (the grid must stay below 2^31 / 256).
 int64_t embedding_blocks(int64_t m, int64_t k);
 

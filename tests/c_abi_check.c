@@ -62,6 +62,11 @@ int main(void) {
   expect("ffn d_model too large",
          ternary_ffn_swiglu(packed, scale, packed, scale, packed, scale, PBG_FFN_MAX_MODEL + 8, 64, x, h, y, 0),
          PBG_ERR_SHAPE);
+  expect("gate_up small m = 9",
+         ternary_swiglu_gate_up_small(packed, scale, packed, scale, 4096, 64, x, PBG_MAX_M + 1, h, 0), PBG_ERR_SHAPE);
+  expect("ffn small null y",
+         ternary_ffn_swiglu_small(packed, scale, packed, scale, packed, scale, 4096, 64, x, 4, h, NULL, 0),
+         PBG_ERR_NULL);
   if (failures == 0) printf("ok\n");
   return failures == 0 ? 0 : 1;
 }

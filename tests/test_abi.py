@@ -132,3 +132,20 @@ def test_ffn_validation():
     assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, None, None) == -1
     assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4100, 12288, GOOD, GOOD, None) == -2
     assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, GOOD + 2, None) == -3
+
+
+def test_ffn_small_validation():
+    lib = binding.lib()
+    p6 = [GOOD] * 6
+    assert lib.ternary_ffn_swiglu_small(None, *p6[1:], 4096, 12288, GOOD, 4, GOOD, GOOD, None) == -1
+    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, 4, GOOD, None, None) == -1
+    for m in (0, 9, -1):
+        assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, m, GOOD, GOOD, None) == -2
+        assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, m, GOOD, None) == -2
+    for dm, dff in ((0, 12288), (4096 + 8, 12288), (100, 12288), (4096, 0)):
+        assert lib.ternary_ffn_swiglu_small(*p6, dm, dff, GOOD, 4, GOOD, GOOD, None) == -2
+    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD + 8, 4, GOOD, GOOD, None) == -3   # x
+    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, 4, GOOD + 2, GOOD, None) == -3   # h
+    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, 4, GOOD, GOOD + 2, None) == -3   # y
+    assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, 4, None, None) == -1
+    assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD + 4, GOOD, 4096, 12288, GOOD, 4, GOOD, None) == -3

@@ -209,3 +209,93 @@ def test_ffn_errors(pbg):
     assert lib.ternary_ffn_swiglu(*args, d_model, d_ff, x.data_ptr(), None, y.data_ptr(), stream) == -1
     for dm, dff in ((100, d_ff), (4104, d_ff), (0, d_ff), (d_model, 0), (d_model, 2 ** 24 + 1)):
         assert lib.ternary_ffn_swiglu(*args, dm, dff, x.data_ptr(), hbuf.data_ptr(), y.data_ptr(), stream) == -2
+
+
+# --------------------------------------------------------------------------
+# The block for 2 <= m <= 8 activation rows (speculative verify)
+# --------------------------------------------------------------------------
+SMALL_SHAPES = [(64, 64), (128, 4160), (256, 1024), (192, 12288 + 64), (4096, 12288)]
+
+
+@pytest.mark.parametrize("m", [2, 3, 5, 8])
+@pytest.mark.parametrize("d_model,d_ff", SMALL_SHAPES)
+def test_ffn_small_exact_probe(pbg, m, d_model, d_ff):
+    """Row i of x is c_i times the integer probe x0 with c_i in {1, -1, 2, -2}: every gate sum is 0 or
+    |g| >= 40, where silu(g) is g or rounds h to zero, so h and y are exact on both sides and equal
+    the oracle bit for bit (the down sums stay below 2^24, checked)."""
+    say(f"ffn small exact m={m} d_model={d_model} d_ff={d_ff}")
+    x0, gate, up, _ = ffn_probe(100 + d_model + d_ff, d_model, d_ff)
+    down = synth.ternary_codes(200 + d_model + d_ff, d_model, d_ff)
+    sd = synth.pow2_scales(300 + d_model, d_model)
+    ones = np.ones(d_ff, dtype=np.float32)
+    gp, upk, dp = oracle.pack(gate)[0], oracle.pack(up)[0], oracle.pack(down)[0]
+    for coef in ([1, -1, 2, -2, 1, 2, -1, -2], [1, -1, 1, -1, -1, 1, 1, -1]):
+        c = np.array(coef[:m], dtype=np.float64)
+        x = (c[:, None] * x0.astype(np.float64)[None, :]).astype(np.float16)
+        h_ref, y_ref = oracle.ffn_swiglu(gp, ones, upk, ones, dp, sd, d_model, x)
+        if np.all(np.abs(down.astype(np.float64)) @ np.abs(h_ref.astype(np.float64)).T < 2 ** 24):
+            break
+    else:
+        pytest.fail("probe sums exceed 2^24")
+    h, y = pbg.ternary_ffn_swiglu(pack(pbg, gate), dev(ones), pack(pbg, up), dev(ones), pack(pbg, down), dev(sd),
+                                  dev(x))
+    assert tuple(h.shape) == (m, d_ff) and tuple(y.shape) == (m, d_model)
+    assert np.array_equal(h_host(h), h_ref.astype(np.float64))
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref)
+    h2 = pbg.ternary_swiglu_gate_up(pack(pbg, gate), dev(ones), pack(pbg, up), dev(ones), d_model, dev(x))
+    assert torch.equal(h2, h)
+
+
+@pytest.mark.parametrize("m", [2, 4, 7, 8])
+@pytest.mark.parametrize("d_model,d_ff", [(128, 4160), (200, 999), (4096, 12288)])
+def test_ffn_small_random_tolerance(pbg, m, d_model, d_ff):
+    """Seeded workload codes and x ~ N(0, 1) rows against the oracle, row by row, with the m = 1 bounds."""
+    say(f"ffn small random m={m} d_model={d_model} d_ff={d_ff}")
+    layer = 1
+    gate = synth.ternary_codes(synth.tensor_seed(layer, "gate") + d_ff, d_ff, d_model, synth.code_dist(layer, "gate"))
+    up = synth.ternary_codes(synth.tensor_seed(layer, "up") + d_ff, d_ff, d_model, synth.code_dist(layer, "up"))
+    down = synth.ternary_codes(synth.tensor_seed(layer, "down") + d_ff, d_model, d_ff,
+                               synth.code_dist(layer, "down"))
+    sg, su, sd = synth.row_scales(611, d_ff), synth.row_scales(612, d_ff), synth.row_scales(613, d_model)
+    x = synth.activations(synth.x_seed(0), m, d_model)
+    gp, upk, dp = oracle.pack(gate)[0], oracle.pack(up)[0], oracle.pack(down)[0]
+    h, y = pbg.ternary_ffn_swiglu(pack(pbg, gate), dev(sg), pack(pbg, up), dev(su), pack(pbg, down), dev(sd), dev(x))
+    h_gpu = h.cpu().numpy()
+    g_ref = oracle.ternary_gemm_small(gp, sg, d_model, x)
+    u_ref = oracle.ternary_gemm_small(upk, su, d_model, x)
+    h_ref = (oracle.silu(g_ref) * u_ref).astype(np.float16)
+    assert_within(h_gpu.astype(np.float64), h_ref.astype(np.float64),
+                  swiglu_h_bound(oracle.silu(g_ref), u_ref, ternary_bound(sg, x), ternary_bound(su, x)), "h")
+    y_down = oracle.ternary_gemm_small(dp, sd, d_ff, h_gpu)
+    assert_within(y.cpu().numpy(), y_down, ternary_bound(sd, h_gpu), "y = down h")
+
+
+def test_ffn_small_graph_replay(pbg):
+    """The m = 8 block captured once and replayed on fresh activations equals eager calls."""
+    d_model, d_ff, m = 4096, 12288, 8
+    say("ffn small graph replay")
+    layer = 3
+    t = {p: pbg.pack_ternary(synth.ternary_codes_device(synth.tensor_seed(layer, p), *synth.SHAPES[p],
+                                                         synth.code_dist(layer, p), "cuda:0"))[0]
+         for p in ("gate", "up", "down")}
+    s = {p: synth.row_scales_device(synth.tensor_seed(layer, p), synth.SHAPES[p][0], "cuda:0")
+         for p in ("gate", "up", "down")}
+    x = dev(synth.activations(801, m, d_model))
+    h = torch.empty((m, d_ff), dtype=torch.float16, device="cuda:0")
+    y = torch.empty((m, d_model), dtype=torch.float32, device="cuda:0")
+    args = (t["gate"], s["gate"], t["up"], s["up"], t["down"], s["down"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pbg.ternary_ffn_swiglu(*args, x, h, y)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pbg.ternary_ffn_swiglu(*args, x, h, y)
+    for rep in range(4):
+        x.copy_(dev(synth.activations(802 + rep, m, d_model)))
+        graph.replay()
+        torch.cuda.synchronize()
+        h_e, y_e = pbg.ternary_ffn_swiglu(*args, x)
+        torch.cuda.synchronize()
+        assert torch.equal(h, h_e) and torch.equal(y, y_e), rep
