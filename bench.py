@@ -405,7 +405,30 @@ def main():
         ms = time_graphs(torch, [g], 5, 1)
         extra["decode_step_fused_m1_us"] = round(ms * 1e3, 1)
         extra["decode_step_fused_m1_GBs"] = round(dec_bytes / (ms * 1e-3) / 1e9, 1)
-        del graphs, g, fused
+        del graphs, g
+
+        # the fused layer at the speculative-verify shapes: q|k|v and o as small-M
+        # GEMMs, the FFN block with m activation rows (gate|up + SwiGLU, then down)
+        yqkv_m = torch.empty((8, fused[0][0].shape[0]), dtype=torch.float32, device=device)
+        h_m = torch.empty((8, synth.FFN), dtype=torch.float16, device=device)
+        y_m = torch.empty((8, synth.HIDDEN), dtype=torch.float32, device=device)
+
+        def fused_layer_m(l, m):
+            qp, qs = fused[l]
+            pbg.ternary_gemm_small(qp, qs, synth.HIDDEN, xs[synth.HIDDEN][:m], yqkv_m[:m])
+            linear(l, "o", m)
+            lay = model.layers[l]
+            pbg.ternary_ffn_swiglu(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], lay["down"][0],
+                                   lay["down"][1], xs[synth.HIDDEN][:m], h_m[:m], y_m[:m])
+
+        for m in (2, 4, 7, 8):
+            graphs = [capture(torch, lambda l=l, m=m: fused_layer_m(l, m)) for l in range(L)]
+            ms = time_graphs(torch, graphs, K, W)
+            lb = sum(ternary_bytes(*synth.SHAPES[p], m) for p in synth.PROJECTIONS)
+            extra[f"layer_fused_m{m}_us"] = round(ms * 1e3, 3)
+            extra[f"layer_fused_m{m}_GBs"] = round(lb / (ms * 1e-3) / 1e9, 1)
+            del graphs
+        del fused, yqkv_m, h_m, y_m
 
         # streaming-read ceiling at the gate byte count: torch copy over a pool
         nbytes = synth.words_bytes(*synth.SHAPES["gate"])

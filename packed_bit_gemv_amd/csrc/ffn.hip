@@ -264,8 +264,10 @@ hipError_t launch_swiglu_gate_up_small(const uint32_t* gate, const float* gate_s
                                        const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x,
                                        int m, uint16_t* h, hipStream_t stream) {
   if (m == 1) return launch_swiglu_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
-  // d_model <= 4,096: at most 16 units of 256 columns, four per wave
-  if (d_ff >= 8192) launch_gate_up_mfma<4, 4, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  // d_model <= 4,096: at most 16 units of 256 columns, four per wave. Tiles per
+  // workgroup from a graph-timed sweep on MI355X (d_ff = 12,288): four, and two
+  // at m = 2 (10.3 against 10.8 us; two separate GEMMs took 12.0 us).
+  if (d_ff >= 8192 && m > 2) launch_gate_up_mfma<4, 4, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   else launch_gate_up_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   return hipGetLastError();
 }
