@@ -14,8 +14,9 @@ Also reported under "extra": the same three linears as three separate GEMV
 launches, microseconds per linear, per decoder layer (7 linears, and with the
 shared-input fusions) and per full decode step (36 layers + int8 head
 151,936 x 4,096), the head alone and with the fused greedy argmax, the
-small-M (speculative verify) shapes, and the streaming ceiling of a plain
-copy (torch) at the same byte count.
+small-M (speculative verify) shapes, including the fused layer and one whole
+verify step at m = 8, the streaming ceiling of a plain copy (torch) at the
+same byte count, and the per-launch floor of a dependent kernel.
 """
 from __future__ import annotations
 
@@ -428,7 +429,20 @@ def main():
             extra[f"layer_fused_m{m}_us"] = round(ms * 1e3, 3)
             extra[f"layer_fused_m{m}_GBs"] = round(lb / (ms * 1e-3) / 1e9, 1)
             del graphs
-        del fused, yqkv_m, h_m, y_m
+
+        # one speculative verify step: 36 fused layers and the greedy token of
+        # each of the 8 rows through the head, one graph
+        def verify_step():
+            for l in range(L):
+                fused_layer_m(l, 8)
+            pbg.int8_head_argmax(hw, hs, xs[hk][:8], keys, tok, lgt)
+
+        g = capture(torch, verify_step)
+        ms = time_graphs(torch, [g], 5, 1)
+        vb = L * sum(ternary_bytes(*synth.SHAPES[p], 8) for p in synth.PROJECTIONS) + head_bytes(hn, hk, 8)
+        extra["verify_step_fused_m8_us"] = round(ms * 1e3, 1)
+        extra["verify_step_fused_m8_GBs"] = round(vb / (ms * 1e-3) / 1e9, 1)
+        del g, fused, yqkv_m, h_m, y_m
 
         # streaming-read ceiling at the gate byte count: torch copy over a pool
         nbytes = synth.words_bytes(*synth.SHAPES["gate"])
