@@ -482,10 +482,11 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
   if (fast && units <= 48) {
     // Launch shapes from sweeps on MI355X at M = 4 and 8: more tiles per
     // workgroup (each activation column reused by more rows) beat more waves,
-    // down to about 192-256 workgroups (n = 12,288: 4 tiles; the q|k|v pack,
-    // n = 6,144: 2 tiles, 5.2 / 6.0 us against 6.7 / 8.4 with 1; n = 4,096: 1).
+    // down to about 192-256 workgroups (n = 12,288: 3 tiles, 6.0-7.0 us
+    // against 6.7-7.5 with 4; the q|k|v pack, n = 6,144: 2 tiles, 5.2 / 6.0 us
+    // at m = 4 / 8 against 6.7 / 8.4 with 1; n = 4,096: 1).
     if (units <= 16) {
-      if (n >= 8192) launch_mfma_cfg<4, 4, 4>(packed, scale, n, k, x, m, y, stream);
+      if (n >= 8192) launch_mfma_cfg<4, 3, 4>(packed, scale, n, k, x, m, y, stream);
       else if (n >= 5120) launch_mfma_cfg<4, 2, 4>(packed, scale, n, k, x, m, y, stream);
       else launch_mfma_cfg<4, 1, 4>(packed, scale, n, k, x, m, y, stream);
     } else if (units <= 32) {
