@@ -136,7 +136,7 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
 // x_j at the 8 columns that A lane (i, g) decodes; partial tiles meet in LDS
 // in wave order. The epilogue forms h = fp16(silu(g) * u) per pair and row of
 // x.
-template <int SK, int T, int UPW>
+template <int SK, int T, int UPW, int MP>
 __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
     const uint4* __restrict__ gate, const float* __restrict__ gate_scale, const uint4* __restrict__ up,
     const float* __restrict__ up_scale, int64_t d_model, int64_t d_ff, int64_t chunks, const uint16_t* __restrict__ x,
@@ -164,13 +164,16 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
     sg[e] = gate_scale[r];
     su[e] = up_scale[r];
   }
-  auto load_unit = [&](int q, uint4 (&xb)[8], uint4 (&wv)[T]) {
+  // x loads are dense for m <= MP, as in the small-M GEMM
+  constexpr int kXLoads = MP / 2, kXSteps = 16 / MP;
+  const int xrow = li % MP, xsub = li / MP;
+  auto load_unit = [&](int q, uint4 (&xb)[kXLoads], uint4 (&wv)[T]) {
     const int64_t u = s + static_cast<int64_t>(SK) * q;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int64_t gi = 32 * u + 8 * lg + v;
-      const bool ok = li < m && gi < groups;
-      xb[v] = xg[ok ? static_cast<int64_t>(li) * groups + gi : 0];
+    for (int a = 0; a < kXLoads; ++a) {
+      const int64_t gi = 32 * u + 8 * lg + a * kXSteps + xsub;
+      const bool ok = xrow < m && gi < groups;
+      xb[a] = xg[ok ? static_cast<int64_t>(xrow) * groups + gi : 0];
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
   float4_t d[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 xb[2][8], wv[2][T];
+  uint4 xb[2][kXLoads], wv[2][T];
   load_unit(0, xb[0], wv[0]);
 #pragma unroll
   for (int q = 0; q < UPW; ++q) {
@@ -193,7 +196,8 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       const int64_t gi = 32 * u + 8 * lg + v;
-      const half8_t b = __builtin_bit_cast(half8_t, masked(xb[q & 1][v], li < m && gi < groups));
+      const uint4 bx = row_take(xb[q & 1][v / kXSteps], (v % kXSteps) * MP);
+      const half8_t b = __builtin_bit_cast(half8_t, masked(bx, gi < groups));
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
@@ -231,13 +235,22 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
   }
 }
 
+template <int SK, int T, int UPW, int MP>
+void launch_gate_up_mp(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
+                       int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((d_ff + 8 * T - 1) / (8 * T)));
+  hipLaunchKernelGGL((swiglu_gate_up_mfma_kernel<SK, T, UPW, MP>), grid, dim3(SK * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(gate), gate_scale, reinterpret_cast<const uint4*>(up), up_scale,
+                     d_model, d_ff, words_per_row(d_model) / 4, x, m, h);
+}
+
+// MP = m rounded up to 2, 4 or 8: the rows one dense x load is laid out for.
 template <int SK, int T, int UPW>
 void launch_gate_up_mfma(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
                          int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((d_ff + 8 * T - 1) / (8 * T)));
-  hipLaunchKernelGGL((swiglu_gate_up_mfma_kernel<SK, T, UPW>), grid, dim3(SK * kWave), 0, stream,
-                     reinterpret_cast<const uint4*>(gate), gate_scale, reinterpret_cast<const uint4*>(up), up_scale,
-                     d_model, d_ff, words_per_row(d_model) / 4, x, m, h);
+  if (m <= 2) launch_gate_up_mp<SK, T, UPW, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  else if (m <= 4) launch_gate_up_mp<SK, T, UPW, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  else launch_gate_up_mp<SK, T, UPW, 8>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
 }
 }  // namespace
 

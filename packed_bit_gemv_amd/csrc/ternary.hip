@@ -290,9 +290,14 @@ __global__ __launch_bounds__(kGemvWaves* kWave) void ternary_gemm_small_kernel(c
 // as 4 operand pairs), and the B lane (g, j) holds x_j at the same 8 columns,
 // so A and B agree on every column whatever order the unit uses inside a
 // K-group. The accumulator lane (g, j) holds rows 4g..4g+3 of column j.
+// Only columns j < M of B matter, so x is loaded densely for M <= MP (MP = 2,
+// 4 or 8): lane (g, j) loads row j % MP of step a * (16 / MP) + j / MP, one
+// load serves 16 / MP steps, and step v rotates the lanes of each 16-lane row
+// so that lane j < MP holds its row's slice (columns j >= MP get another
+// step's data and are discarded).
 // A workgroup holds SK waves that split the units of T tiles; their partial
 // tiles meet in LDS and are added in wave order.
-template <int SK, int T, int UPW>
+template <int SK, int T, int UPW, int MP>
 __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint4* __restrict__ packed,
                                                                        const float* __restrict__ scale,
                                                                        int64_t n, int64_t k, int64_t chunks,
@@ -320,15 +325,18 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
     sc[e] = scale[r < n ? r : n - 1];
   }
 
-  // Loads of one unit: the B operands x_j of this lane's columns (zero for
-  // j >= m or past k) and one 16-byte chunk of A per tile.
-  auto load_unit = [&](int q, uint4 (&xb)[8], uint4 (&wv)[T]) {
+  // Loads of one unit: MP / 2 dense loads of x (rows past m and groups past k
+  // read x[0..7] and are masked or discarded at use) and one 16-byte chunk of
+  // A per tile.
+  constexpr int kXLoads = MP / 2, kXSteps = 16 / MP;
+  const int xrow = li % MP, xsub = li / MP;
+  auto load_unit = [&](int q, uint4 (&xb)[kXLoads], uint4 (&wv)[T]) {
     const int64_t u = s + static_cast<int64_t>(SK) * q;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int64_t gi = 32 * u + 8 * lg + v;  // 8-column group within a row of x
-      const bool ok = li < m && gi < groups;
-      xb[v] = xg[ok ? static_cast<int64_t>(li) * groups + gi : 0];
+    for (int a = 0; a < kXLoads; ++a) {
+      const int64_t gi = 32 * u + 8 * lg + a * kXSteps + xsub;  // 8-column group within a row of x
+      const bool ok = xrow < m && gi < groups;
+      xb[a] = xg[ok ? static_cast<int64_t>(xrow) * groups + gi : 0];
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
   float4_t d[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 xb[2][8], wv[2][T];
+  uint4 xb[2][kXLoads], wv[2][T];
   load_unit(0, xb[0], wv[0]);
 #pragma unroll
   for (int q = 0; q < UPW; ++q) {
@@ -351,14 +359,9 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
     const int64_t u = s + static_cast<int64_t>(SK) * q;
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      uint4 bx = xb[q & 1][v];
       const int64_t gi = 32 * u + 8 * lg + v;
-      const uint32_t keep = (li < m && gi < groups) ? 0xFFFFFFFFu : 0u;
-      bx.x &= keep;
-      bx.y &= keep;
-      bx.z &= keep;
-      bx.w &= keep;
-      const half8_t b = __builtin_bit_cast(half8_t, bx);
+      const uint4 bx = row_take(xb[q & 1][v / kXSteps], (v % kXSteps) * MP);
+      const half8_t b = __builtin_bit_cast(half8_t, masked(bx, gi < groups));
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
@@ -400,12 +403,21 @@ void launch_rows_cfg(const uint32_t* packed, const float* scale, int64_t n, int6
                      reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, y);
 }
 
+template <int SK, int T, int UPW, int MP>
+void launch_mfma_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
+                    float* y, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
+  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP>), grid, dim3(SK * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y);
+}
+
+// MP = m rounded up to 2, 4 or 8: the rows one dense x load is laid out for.
 template <int SK, int T, int UPW>
 void launch_mfma_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
                      float* y, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
-  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW>), grid, dim3(SK * kWave), 0, stream,
-                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y);
+  if (m <= 2) launch_mfma_mp<SK, T, UPW, 2>(packed, scale, n, k, x, m, y, stream);
+  else if (m <= 4) launch_mfma_mp<SK, T, UPW, 4>(packed, scale, n, k, x, m, y, stream);
+  else launch_mfma_mp<SK, T, UPW, 8>(packed, scale, n, k, x, m, y, stream);
 }
 
 template <int M>
@@ -461,17 +473,11 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
   const int64_t cpl = (words_per_row(k) / 4 + kWave - 1) / kWave;  // chunks per lane of the M-row kernel
   const bool fast = k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   // Shared decode on the VALU where it beat the matrix cores in graph-timed
-  // sweeps on MI355X: M = 2 up to 12,288 columns, M = 3 for short K and N.
-  if (fast && m == 2 && cpl <= 3) {
-    if (cpl == 1) {
-      if (n >= 8192) launch_rows_cfg<1, 4, 3, 2>(packed, scale, n, k, x, y, stream);
-      else if (n >= 2048) launch_rows_cfg<1, 8, 1, 2>(packed, scale, n, k, x, y, stream);
-      else launch_rows_cfg<1, 4, 1, 2>(packed, scale, n, k, x, y, stream);
-    } else if (cpl == 2) {
-      launch_rows_cfg<2, 8, 1, 2>(packed, scale, n, k, x, y, stream);
-    } else {
-      launch_rows_cfg<3, 8, 1, 2>(packed, scale, n, k, x, y, stream);
-    }
+  // sweeps on MI355X: M = 2 for K <= 4,096 and N < 8,192 (q|k|v pack, q, k),
+  // M = 3 for K <= 4,096 and N < 2,048.
+  if (fast && m == 2 && cpl == 1 && n < 8192) {
+    if (n >= 2048) launch_rows_cfg<1, 8, 1, 2>(packed, scale, n, k, x, y, stream);
+    else launch_rows_cfg<1, 4, 1, 2>(packed, scale, n, k, x, y, stream);
     return hipGetLastError();
   }
   if (fast && m == 3 && cpl == 1 && n < 2048) {
@@ -480,17 +486,28 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
   }
   const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
   if (fast && units <= 48) {
-    // Launch shapes from sweeps on MI355X at M = 4 and 8: more tiles per
-    // workgroup (each activation column reused by more rows) beat more waves,
-    // down to about 192-256 workgroups (n = 12,288: 3 tiles, 6.0-7.0 us
-    // against 6.7-7.5 with 4; the q|k|v pack, n = 6,144: 2 tiles, 5.2 / 6.0 us
-    // at m = 4 / 8 against 6.7 / 8.4 with 1; n = 4,096: 1).
+    // Launch shapes from graph-timed sweeps on MI355X at M = 3, 4 and 8.
+    // More tiles per workgroup (each activation column reused by more rows)
+    // beat more waves down to about 192-256 workgroups; at M <= 4 the dense
+    // x loads leave registers for 8-16 waves per workgroup, which wins.
+    // n = 12,288: 3 tiles (5.7-6.5 us; 4 tiles 6.3-7.1); the q|k|v pack,
+    // n = 6,144: 2 tiles (4.7-5.5 us; 1 tile 5.3-7.4); n = 4,096: 1 tile;
+    // K = 8,192 and 12,288: 8 waves at M <= 4 (K = 12,288: 6.5-7.1 us
+    // against 8.0-8.1 with 4; the M = 2 rows kernel took 7.1). At M = 2 and
+    // n = 12,288, 16 waves: 5.5 us (rows kernel 6.1).
     if (units <= 16) {
-      if (n >= 8192) launch_mfma_cfg<4, 3, 4>(packed, scale, n, k, x, m, y, stream);
+      if (n >= 8192 && m == 2) launch_mfma_cfg<16, 3, 1>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 8192) launch_mfma_cfg<4, 3, 4>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 5120 && m <= 4) launch_mfma_cfg<8, 2, 2>(packed, scale, n, k, x, m, y, stream);
       else if (n >= 5120) launch_mfma_cfg<4, 2, 4>(packed, scale, n, k, x, m, y, stream);
+      else if (m <= 4) launch_mfma_cfg<16, 1, 1>(packed, scale, n, k, x, m, y, stream);
       else launch_mfma_cfg<4, 1, 4>(packed, scale, n, k, x, m, y, stream);
+    } else if (units <= 32 && m <= 4) {
+      launch_mfma_cfg<8, 1, 4>(packed, scale, n, k, x, m, y, stream);
     } else if (units <= 32) {
       launch_mfma_cfg<4, 1, 8>(packed, scale, n, k, x, m, y, stream);
+    } else if (m <= 4) {
+      launch_mfma_cfg<8, 1, 6>(packed, scale, n, k, x, m, y, stream);
     } else {
       launch_mfma_cfg<4, 1, 12>(packed, scale, n, k, x, m, y, stream);
     }
