@@ -280,8 +280,8 @@ hipError_t launch_swiglu_gate_up_small(const uint32_t* gate, const float* gate_s
   // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from
   // graph-timed sweeps on MI355X at d_ff = 12,288: six tiles (48 pairs, 256
   // workgroups) per workgroup, with 8 waves of two units each up to m = 4
-  // (8.4-8.7 us) and 4 waves of four units beyond (10.2 us at m = 8); four
-  // tiles took 10.8-12.8 us and two separate GEMMs 12.0-14.9 us.
+  // (8.35-8.8 us) and 4 waves of four units beyond (9.4 us at m = 8); four
+  // tiles took 9.6-12.0 us.
   if (d_ff >= 8192) {
     if (m <= 4) launch_gate_up_mfma<8, 6, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
     else launch_gate_up_mfma<4, 6, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
