@@ -164,21 +164,32 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
     sg[e] = gate_scale[r];
     su[e] = up_scale[r];
   }
-  // x loads are dense for m <= MP, as in the small-M GEMM
-  constexpr int kXLoads = MP / 2, kXSteps = 16 / MP;
-  const int xrow = li % MP, xsub = li / MP;
-  auto load_unit = [&](int q, uint4 (&xb)[kXLoads], uint4 (&wv)[T]) {
+  // x: line-wise loads staged through this wave's LDS slice, as in the
+  // small-M GEMM
+  constexpr int kXLoads = MP / 2;
+  constexpr int kSlots = 33;  // 16-byte slots per row and unit, one of padding
+  __shared__ uint4 xs[SK][2][MP * kSlots];
+  const int xrow = li >> 3, xg8 = li & 7;
+  auto load_x = [&](int q, uint4 (&xr)[kXLoads]) {
     const int64_t u = s + static_cast<int64_t>(SK) * q;
 #pragma unroll
     for (int a = 0; a < kXLoads; ++a) {
-      const int64_t gi = 32 * u + 8 * lg + a * kXSteps + xsub;
-      const bool ok = xrow < m && gi < groups;
-      xb[a] = xg[ok ? static_cast<int64_t>(xrow) * groups + gi : 0];
+      const int row = 2 * a + xrow;
+      const int64_t gi = 32 * u + 8 * lg + xg8;
+      xr[a] = xg[row < m && gi < groups ? static_cast<int64_t>(row) * groups + gi : 0];
     }
+  };
+  auto stage_x = [&](int q, const uint4 (&xr)[kXLoads]) {
+    const int64_t gi = 32 * (s + static_cast<int64_t>(SK) * q) + 8 * lg + xg8;
+#pragma unroll
+    for (int a = 0; a < kXLoads; ++a)
+      xs[s][q & 1][(2 * a + xrow) * kSlots + 8 * lg + xg8] = masked(xr[a], gi < groups);
+  };
+  auto load_w = [&](int q, uint4 (&wv)[T]) {
+    const int64_t c = 4 * (s + static_cast<int64_t>(SK) * q) + lg;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t r = pair_base + 8 * t + (li & 7);
-      const int64_t c = 4 * u + lg;
       wv[t] = load_nt(src + (r < d_ff ? r : d_ff - 1) * chunks + (c < chunks ? c : chunks - 1));
     }
   };
@@ -186,18 +197,21 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
   float4_t d[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 xb[2][kXLoads], wv[2][T];
-  load_unit(0, xb[0], wv[0]);
+  uint4 xr[kXLoads], wv[2][T];
+  load_x(0, xr);
+  load_w(0, wv[0]);
+  stage_x(0, xr);
+  if (UPW > 1) {
+    load_x(1, xr);
+    load_w(1, wv[1]);
+  }
+  const int brow = (li % MP) * kSlots + 8 * lg;
 #pragma unroll
   for (int q = 0; q < UPW; ++q) {
-    if (q + 1 < UPW) load_unit(q + 1, xb[(q + 1) & 1], wv[(q + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t u = s + static_cast<int64_t>(SK) * q;
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      const int64_t gi = 32 * u + 8 * lg + v;
-      const uint4 bx = row_take(xb[q & 1][v / kXSteps], (v % kXSteps) * MP);
-      const half8_t b = __builtin_bit_cast(half8_t, masked(bx, gi < groups));
+      const half8_t b = __builtin_bit_cast(half8_t, xs[s][q & 1][brow + v]);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
@@ -205,6 +219,13 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
         const uint4 ap = make_uint4(code_pair(wd, 4 * hh + 0), code_pair(wd, 4 * hh + 1), code_pair(wd, 4 * hh + 2),
                                     code_pair(wd, 4 * hh + 3));
         d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
+      }
+    }
+    if (q + 1 < UPW) {
+      stage_x(q + 1, xr);
+      if (q + 2 < UPW) {
+        load_x(q + 2, xr);
+        load_w(q + 2, wv[q & 1]);
       }
     }
   }
@@ -278,13 +299,13 @@ hipError_t launch_swiglu_gate_up_small(const uint32_t* gate, const float* gate_s
                                        int m, uint16_t* h, hipStream_t stream) {
   if (m == 1) return launch_swiglu_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
   // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from
-  // graph-timed sweeps on MI355X at d_ff = 12,288: six tiles (48 pairs, 256
-  // workgroups) per workgroup, with 8 waves of two units each up to m = 4
-  // (8.35-8.8 us) and 4 waves of four units beyond (9.4 us at m = 8); four
-  // tiles took 9.6-12.0 us.
-  if (d_ff >= 8192) {
-    if (m <= 4) launch_gate_up_mfma<8, 6, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-    else launch_gate_up_mfma<4, 6, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  // graph-timed sweeps on MI355X at d_ff = 12,288: three tiles (24 pairs, 512
+  // workgroups) of 4 waves up to m = 4 (7.7-8.2 us), six tiles of 8 waves
+  // beyond (8.9 us at m = 8); four tiles took 9.3-10.6 us.
+  if (d_ff >= 8192 && m <= 4) {
+    launch_gate_up_mfma<4, 3, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  } else if (d_ff >= 8192) {
+    launch_gate_up_mp<8, 6, 2, 8>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   } else {
     launch_gate_up_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   }

@@ -132,39 +132,6 @@ __device__ __forceinline__ float row_ror(float v) {
   return as_f32(__builtin_amdgcn_update_dpp(0u, as_u32(v), 0x120 + N, 0xF, 0xF, false));
 }
 
-// Lane j of every 16-lane row takes the 16 bytes held by lane (j + n) mod 16
-// of its row: a DPP row rotation, registers only. n is a constant once the
-// caller's loops are unrolled, so the switch folds to at most four moves.
-template <int R>
-__device__ __forceinline__ uint4 row_rotate(const uint4& v) {
-  return make_uint4(__builtin_amdgcn_update_dpp(0u, v.x, 0x120 + R, 0xF, 0xF, false),
-                    __builtin_amdgcn_update_dpp(0u, v.y, 0x120 + R, 0xF, 0xF, false),
-                    __builtin_amdgcn_update_dpp(0u, v.z, 0x120 + R, 0xF, 0xF, false),
-                    __builtin_amdgcn_update_dpp(0u, v.w, 0x120 + R, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ uint4 row_take(const uint4& v, int n) {
-  // row_ror:r gives lane j the value of lane (j - r) mod 16
-  switch (n & 15) {
-    case 1: return row_rotate<15>(v);
-    case 2: return row_rotate<14>(v);
-    case 3: return row_rotate<13>(v);
-    case 4: return row_rotate<12>(v);
-    case 5: return row_rotate<11>(v);
-    case 6: return row_rotate<10>(v);
-    case 7: return row_rotate<9>(v);
-    case 8: return row_rotate<8>(v);
-    case 9: return row_rotate<7>(v);
-    case 10: return row_rotate<6>(v);
-    case 11: return row_rotate<5>(v);
-    case 12: return row_rotate<4>(v);
-    case 13: return row_rotate<3>(v);
-    case 14: return row_rotate<2>(v);
-    case 15: return row_rotate<1>(v);
-    default: return v;
-  }
-}
-
 // Sum of a value over the 16 lanes of each row; every lane gets its row's sum.
 __device__ __forceinline__ float row_sum16(float v) {
   v += row_ror<8>(v);

@@ -290,11 +290,12 @@ __global__ __launch_bounds__(kGemvWaves* kWave) void ternary_gemm_small_kernel(c
 // as 4 operand pairs), and the B lane (g, j) holds x_j at the same 8 columns,
 // so A and B agree on every column whatever order the unit uses inside a
 // K-group. The accumulator lane (g, j) holds rows 4g..4g+3 of column j.
-// Only columns j < M of B matter, so x is loaded densely for M <= MP (MP = 2,
-// 4 or 8): lane (g, j) loads row j % MP of step a * (16 / MP) + j / MP, one
-// load serves 16 / MP steps, and step v rotates the lanes of each 16-lane row
-// so that lane j < MP holds its row's slice (columns j >= MP get another
-// step's data and are discarded).
+// Only columns j < M <= MP of B matter (MP = 2, 4 or 8). x is loaded a whole
+// 128-byte line at a time: load a of a unit gives lane-group g the line of
+// groups 8g..8g+7 for rows 2a and 2a + 1, so MP / 2 loads cover the unit. A
+// per-wave LDS slice (MP rows of 32 16-byte slots plus one of padding, two
+// buffers) turns that into the B layout: step v reads slot 8g + v of row
+// j mod MP, conflict-free. Columns j >= M are discarded in the epilogue.
 // A workgroup holds SK waves that split the units of T tiles; their partial
 // tiles meet in LDS and are added in wave order.
 template <int SK, int T, int UPW, int MP>
@@ -325,23 +326,34 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
     sc[e] = scale[r < n ? r : n - 1];
   }
 
-  // Loads of one unit: MP / 2 dense loads of x (rows past m and groups past k
-  // read x[0..7] and are masked or discarded at use) and one 16-byte chunk of
-  // A per tile.
-  constexpr int kXLoads = MP / 2, kXSteps = 16 / MP;
-  const int xrow = li % MP, xsub = li / MP;
-  auto load_unit = [&](int q, uint4 (&xb)[kXLoads], uint4 (&wv)[T]) {
+  // x of one 256-column unit: MP / 2 line-wise loads, staged through this
+  // wave's LDS slice. Rows past m read x[0..7] (their columns are discarded)
+  // and groups past k are zeroed when staged.
+  constexpr int kXLoads = MP / 2;
+  constexpr int kSlots = 33;  // 16-byte slots per row and unit, one of padding
+  __shared__ uint4 xs[SK][2][MP * kSlots];
+  const int xrow = li >> 3, xg8 = li & 7;
+  auto load_x = [&](int q, uint4 (&xr)[kXLoads]) {
     const int64_t u = s + static_cast<int64_t>(SK) * q;
 #pragma unroll
     for (int a = 0; a < kXLoads; ++a) {
-      const int64_t gi = 32 * u + 8 * lg + a * kXSteps + xsub;  // 8-column group within a row of x
-      const bool ok = xrow < m && gi < groups;
-      xb[a] = xg[ok ? static_cast<int64_t>(xrow) * groups + gi : 0];
+      const int row = 2 * a + xrow;
+      const int64_t gi = 32 * u + 8 * lg + xg8;  // 8-column group within a row of x
+      xr[a] = xg[row < m && gi < groups ? static_cast<int64_t>(row) * groups + gi : 0];
     }
+  };
+  auto stage_x = [&](int q, const uint4 (&xr)[kXLoads]) {
+    const int64_t gi = 32 * (s + static_cast<int64_t>(SK) * q) + 8 * lg + xg8;
+#pragma unroll
+    for (int a = 0; a < kXLoads; ++a)
+      xs[s][q & 1][(2 * a + xrow) * kSlots + 8 * lg + xg8] = masked(xr[a], gi < groups);
+  };
+  // one 16-byte chunk of A per tile
+  auto load_w = [&](int q, uint4 (&wv)[T]) {
+    const int64_t c = 4 * (s + static_cast<int64_t>(SK) * q) + lg;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t r = row_base + 16 * t + li;
-      const int64_t c = 4 * u + lg;
       wv[t] = load_nt(packed + (r < n ? r : n - 1) * chunks + (c < chunks ? c : chunks - 1));
     }
   };
@@ -349,19 +361,23 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
   float4_t d[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 xb[2][kXLoads], wv[2][T];
-  load_unit(0, xb[0], wv[0]);
+  // unit q + 1's loads are in flight while unit q is decoded; its x is
+  // staged after unit q's last MFMA
+  uint4 xr[kXLoads], wv[2][T];
+  load_x(0, xr);
+  load_w(0, wv[0]);
+  stage_x(0, xr);
+  if (UPW > 1) {
+    load_x(1, xr);
+    load_w(1, wv[1]);
+  }
+  const int brow = (li % MP) * kSlots + 8 * lg;  // B slots of this lane (lanes j >= MP repeat a row)
 #pragma unroll
   for (int q = 0; q < UPW; ++q) {
-    // the next unit's loads go out before this unit is decoded
-    if (q + 1 < UPW) load_unit(q + 1, xb[(q + 1) & 1], wv[(q + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t u = s + static_cast<int64_t>(SK) * q;
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      const int64_t gi = 32 * u + 8 * lg + v;
-      const uint4 bx = row_take(xb[q & 1][v / kXSteps], (v % kXSteps) * MP);
-      const half8_t b = __builtin_bit_cast(half8_t, masked(bx, gi < groups));
+      const half8_t b = __builtin_bit_cast(half8_t, xs[s][q & 1][brow + v]);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
@@ -369,6 +385,13 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
         const uint4 ap = make_uint4(code_pair(wd, 4 * h + 0), code_pair(wd, 4 * h + 1), code_pair(wd, 4 * h + 2),
                                     code_pair(wd, 4 * h + 3));
         d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
+      }
+    }
+    if (q + 1 < UPW) {
+      stage_x(q + 1, xr);
+      if (q + 2 < UPW) {
+        load_x(q + 2, xr);
+        load_w(q + 2, wv[q & 1]);
       }
     }
   }
@@ -411,7 +434,7 @@ void launch_mfma_mp(const uint32_t* packed, const float* scale, int64_t n, int64
                      reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y);
 }
 
-// MP = m rounded up to 2, 4 or 8: the rows one dense x load is laid out for.
+// MP = m rounded up to 2, 4 or 8: the activation rows one x slice holds.
 template <int SK, int T, int UPW>
 void launch_mfma_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
                      float* y, hipStream_t stream) {
@@ -473,43 +496,32 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
   const int64_t cpl = (words_per_row(k) / 4 + kWave - 1) / kWave;  // chunks per lane of the M-row kernel
   const bool fast = k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   // Shared decode on the VALU where it beat the matrix cores in graph-timed
-  // sweeps on MI355X: M = 2 for K <= 4,096 and N < 8,192 (q|k|v pack, q, k),
-  // M = 3 for K <= 4,096 and N < 2,048.
-  if (fast && m == 2 && cpl == 1 && n < 8192) {
-    if (n >= 2048) launch_rows_cfg<1, 8, 1, 2>(packed, scale, n, k, x, y, stream);
-    else launch_rows_cfg<1, 4, 1, 2>(packed, scale, n, k, x, y, stream);
-    return hipGetLastError();
-  }
-  if (fast && m == 3 && cpl == 1 && n < 2048) {
-    launch_rows_cfg<1, 4, 1, 3>(packed, scale, n, k, x, y, stream);
+  // sweeps on MI355X: M = 2 and 3 for K <= 4,096 and N < 2,048 (k, v).
+  if (fast && (m == 2 || m == 3) && cpl == 1 && n < 2048) {
+    if (m == 2) launch_rows_cfg<1, 4, 1, 2>(packed, scale, n, k, x, y, stream);
+    else launch_rows_cfg<1, 4, 1, 3>(packed, scale, n, k, x, y, stream);
     return hipGetLastError();
   }
   const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
   if (fast && units <= 48) {
-    // Launch shapes from graph-timed sweeps on MI355X at M = 3, 4 and 8.
-    // More tiles per workgroup (each activation column reused by more rows)
-    // beat more waves down to about 192-256 workgroups; at M <= 4 the dense
-    // x loads leave registers for 8-16 waves per workgroup, which wins.
-    // n = 12,288: 3 tiles (5.7-6.5 us; 4 tiles 6.3-7.1); the q|k|v pack,
-    // n = 6,144: 2 tiles (4.7-5.5 us; 1 tile 5.3-7.4); n = 4,096: 1 tile;
-    // K = 8,192 and 12,288: 8 waves at M <= 4 (K = 12,288: 6.5-7.1 us
-    // against 8.0-8.1 with 4; the M = 2 rows kernel took 7.1). At M = 2 and
-    // n = 12,288, 16 waves: 5.5 us (rows kernel 6.1).
+    // Launch shapes from graph-timed sweeps on MI355X at M = 2..8. More tiles
+    // per workgroup (each activation column reused by more rows) beat more
+    // waves down to about 192-256 workgroups. n = 12,288: 3 tiles (5.6-6.2
+    // us); the q|k|v pack, n = 6,144: 2 tiles (4.4-4.9 us), at m = 2 one
+    // tile and 16 waves (4.3 us); n = 4,096: one tile, 16 waves at m = 3, 4
+    // (3.7 us) and 8 otherwise (3.4 us at m = 2, 3.9 at m = 8); K = 8,192
+    // and 12,288: 8 waves (4.4-5.5 and 6.0-7.6 us; 4 waves 5.0-6.0 and
+    // 6.6-8.0).
     if (units <= 16) {
-      if (n >= 8192 && m == 2) launch_mfma_cfg<16, 3, 1>(packed, scale, n, k, x, m, y, stream);
-      else if (n >= 8192) launch_mfma_cfg<4, 3, 4>(packed, scale, n, k, x, m, y, stream);
-      else if (n >= 5120 && m <= 4) launch_mfma_cfg<8, 2, 2>(packed, scale, n, k, x, m, y, stream);
+      if (n >= 8192) launch_mfma_cfg<4, 3, 4>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 5120 && m == 2) launch_mfma_mp<16, 1, 1, 2>(packed, scale, n, k, x, m, y, stream);
       else if (n >= 5120) launch_mfma_cfg<4, 2, 4>(packed, scale, n, k, x, m, y, stream);
-      else if (m <= 4) launch_mfma_cfg<16, 1, 1>(packed, scale, n, k, x, m, y, stream);
-      else launch_mfma_cfg<4, 1, 4>(packed, scale, n, k, x, m, y, stream);
-    } else if (units <= 32 && m <= 4) {
-      launch_mfma_cfg<8, 1, 4>(packed, scale, n, k, x, m, y, stream);
+      else if (m == 3 || m == 4) launch_mfma_mp<16, 1, 1, 4>(packed, scale, n, k, x, m, y, stream);
+      else launch_mfma_cfg<8, 1, 2>(packed, scale, n, k, x, m, y, stream);
     } else if (units <= 32) {
-      launch_mfma_cfg<4, 1, 8>(packed, scale, n, k, x, m, y, stream);
-    } else if (m <= 4) {
-      launch_mfma_cfg<8, 1, 6>(packed, scale, n, k, x, m, y, stream);
+      launch_mfma_cfg<8, 1, 4>(packed, scale, n, k, x, m, y, stream);
     } else {
-      launch_mfma_cfg<4, 1, 12>(packed, scale, n, k, x, m, y, stream);
+      launch_mfma_cfg<8, 1, 6>(packed, scale, n, k, x, m, y, stream);
     }
     return hipGetLastError();
   }
