@@ -265,7 +265,7 @@ void launch_gate_up_mp(const uint32_t* gate, const float* gate_scale, const uint
                      d_model, d_ff, words_per_row(d_model) / 4, x, m, h);
 }
 
-// MP = m rounded up to 2, 4 or 8: the rows one dense x load is laid out for.
+// MP = m rounded up to 2, 4 or 8: the activation rows one x slice holds.
 template <int SK, int T, int UPW>
 void launch_gate_up_mfma(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
                          int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {

@@ -125,8 +125,8 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
 __device__ __forceinline__ uint32_t as_u32(float v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ float as_f32(uint32_t v) { return __builtin_bit_cast(float, v); }
 
-// DPP row rotate: every lane reads the lane `n` places to its right within its
-// 16-lane row.
+// DPP row rotate: lane j of every 16-lane row reads lane (j - N) mod 16 of
+// that row.
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
   return as_f32(__builtin_amdgcn_update_dpp(0u, as_u32(v), 0x120 + N, 0xF, 0xF, false));
