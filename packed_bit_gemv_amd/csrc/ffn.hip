@@ -14,8 +14,8 @@
 // Work split of launch 1: a wave owns R consecutive row pairs (gate row r and
 // up row r) and reads 16-byte chunk `lane` (64 codes) of each; x is staged
 // through LDS like the M = 1 GEMV. The 2R row sums are reduced four at a time
-// across the wave, read back as uniform values, and lane 0 writes the R fp16
-// results with one store.
+// across the wave, lane i < R gathers the gate and up sums of pair i, and
+// those lanes form and store the R fp16 results.
 #include "pbg_device.hpp"
 #include "pbg_internal.hpp"
 
@@ -42,7 +42,10 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t groups = d_model / 8;
-  const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * G + wave) * R;  // first row pair
+  // first row pair: the waves of a workgroup take pairs far apart (wave w of
+  // block b owns pairs (w * blocks + b) * R ..), which evens out when their
+  // weights arrive
+  const int64_t r0 = (static_cast<int64_t>(wave) * gridDim.x + blockIdx.x) * R;
   const uint4* xg = reinterpret_cast<const uint4*>(x);
 
   // activations first, then every weight load of the wave
@@ -97,45 +100,18 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
 #pragma unroll
   for (int q = 0; q < kRed; ++q) red[q] = wave_reduce4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
 
-  constexpr int kSlotLane[4] = {0, 32, 16, 48};  // lane holding operand 0..3 of wave_reduce4
-  uint32_t bits[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const float g = as_f32(__builtin_amdgcn_readlane(as_u32(red[i / 4]), kSlotLane[i % 4]));
-    const float u = as_f32(__builtin_amdgcn_readlane(as_u32(red[(R + i) / 4]), kSlotLane[(R + i) % 4]));
-    const float gs = as_f32(__builtin_amdgcn_readlane(as_u32(sg), i));
-    const float us = as_f32(__builtin_amdgcn_readlane(as_u32(su), i));
-    const float hv = silu(g * (gs * kCodeUnitInv)) * (u * (us * kCodeUnitInv));
-    bits[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
-  }
-  if (lane == 0) {
-    if (r0 + R <= d_ff) {
-      if constexpr (R == 1) {
-        h[r0] = static_cast<uint16_t>(bits[0]);
-      } else if constexpr (R == 2) {
-        *reinterpret_cast<uint32_t*>(h + r0) = bits[0] | (bits[1] << 16);
-      } else {
-        *reinterpret_cast<uint2*>(h + r0) = make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-        if (r0 + i < d_ff) h[r0 + i] = static_cast<uint16_t>(bits[i]);
-    }
-  }
+  // Lane i < R forms pair i: its gate sum is operand i of the reductions and
+  // its up sum operand R + i; wave_reduce4 leaves operands 0..3 in lanes 0,
+  // 32, 16, 48, and the register holding them is the same for every pair
+  // (R <= 4). Lane i already holds the scales of pair i.
+  const int pi = lane < R ? lane : 0;
+  auto slot_lane = [](int i) { return (i & 1) * 32 + ((i >> 1) & 1) * 16; };  // 0, 32, 16, 48
+  const float g = __shfl(red[0], slot_lane(pi), kWave);
+  const float u = __shfl(red[R / 4], slot_lane(R + pi), kWave);
+  const float hv = silu(g * (sg * kCodeUnitInv)) * (u * (su * kCodeUnitInv));
+  if (lane < R && r0 + lane < d_ff) h[r0 + lane] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
 }
 
-
-// 2 <= M <= 8 activation rows (d_model % 8 == 0, x 16-byte aligned): the same
-// launch on the matrix cores. A 16-row MFMA tile holds 8 gate rows and the
-// same 8 up rows: lane (i, g) reads gate row p0 + i for i < 8 and up row
-// p0 + i - 8 otherwise, so accumulator lanes g = 0, 1 end with the gate sums
-// of the 8 pairs and g = 2, 3 with their up sums, per activation column j.
-// The rest follows the small-M GEMM (ternary.hip): SK waves split the
-// 256-column units of T tiles, one unit's loads ahead; B lane (g, j) holds
-// x_j at the 8 columns that A lane (i, g) decodes; partial tiles meet in LDS
-// in wave order. The epilogue forms h = fp16(silu(g) * u) per pair and row of
-// x.
 template <int SK, int T, int UPW, int MP>
 __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
     const uint4* __restrict__ gate, const float* __restrict__ gate_scale, const uint4* __restrict__ up,
