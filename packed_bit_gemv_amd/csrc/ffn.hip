@@ -42,10 +42,7 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t groups = d_model / 8;
-  // first row pair: the waves of a workgroup take pairs far apart (wave w of
-  // block b owns pairs (w * blocks + b) * R ..), which evens out when their
-  // weights arrive
-  const int64_t r0 = (static_cast<int64_t>(wave) * gridDim.x + blockIdx.x) * R;
+  const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * G + wave) * R;  // first row pair
   const uint4* xg = reinterpret_cast<const uint4*>(x);
 
   // activations first, then every weight load of the wave
