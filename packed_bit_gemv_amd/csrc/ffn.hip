@@ -14,8 +14,8 @@
 // Work split of launch 1: a wave owns R consecutive row pairs (gate row r and
 // up row r) and reads 16-byte chunk `lane` (64 codes) of each; x is staged
 // through LDS like the M = 1 GEMV. The 2R row sums are reduced four at a time
-// across the wave, lane i < R gathers the gate and up sums of pair i, and
-// those lanes form and store the R fp16 results.
+// across the wave, one lane swap puts each gate sum beside its up sum, and
+// two lanes per reduction form and store the fp16 results.
 #include "pbg_device.hpp"
 #include "pbg_internal.hpp"
 
@@ -37,7 +37,6 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
   static_assert(R == 1 || R == 2 || R == 4, "R pairs fill whole reductions");
   constexpr int kThreads = G * kWave;
   constexpr int kX = kWave * 8;  // 16-byte activation groups of one 4,096-column slice
-  constexpr int kRed = (2 * R + 3) / 4;
   __shared__ uint4 buf[kX];      // group (c, q) at q * 64 + c
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -64,9 +63,16 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
     wg[i] = load_nt(gate + r * chunks + cl);
     wu[i] = load_nt(up + r * chunks + cl);
   }
-  const int64_t rs = r0 + (lane < R ? lane : 0);
-  const float sg = gate_scale[rs < d_ff ? rs : d_ff - 1];
-  const float su = up_scale[rs < d_ff ? rs : d_ff - 1];
+  // lanes 0 and 16 form pairs 2q and 2q + 1 of reduction q (below); their scales
+  constexpr int kRed = (2 * R + 3) / 4;
+  const int half = (lane >> 4) & 1;
+  float sg[kRed], su[kRed];
+#pragma unroll
+  for (int q = 0; q < kRed; ++q) {
+    const int64_t rs = r0 + (2 * q + half < R ? 2 * q + half : 0);
+    sg[q] = gate_scale[rs < d_ff ? rs : d_ff - 1];
+    su[q] = up_scale[rs < d_ff ? rs : d_ff - 1];
+  }
   __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -85,28 +91,31 @@ __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
     xp[4 * q + 3] = v.w;
   }
 
-  float acc[4 * kRed];  // gate sums of the R pairs, then their up sums
+  float acc[4 * kRed];  // per reduction q: gate and up sums of pair 2q, then of pair 2q + 1
 #pragma unroll
   for (int i = 0; i < 4 * kRed; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    acc[i] = chunk_dot(wg[i], xp, 0.0f);
-    acc[R + i] = chunk_dot(wu[i], xp, 0.0f);
+    acc[4 * (i / 2) + 2 * (i % 2)] = chunk_dot(wg[i], xp, 0.0f);
+    acc[4 * (i / 2) + 2 * (i % 2) + 1] = chunk_dot(wu[i], xp, 0.0f);
   }
   float red[kRed];
 #pragma unroll
   for (int q = 0; q < kRed; ++q) red[q] = wave_reduce4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
 
-  // Lane i < R forms pair i: its gate sum is operand i of the reductions and
-  // its up sum operand R + i; wave_reduce4 leaves operands 0..3 in lanes 0,
-  // 32, 16, 48, and the register holding them is the same for every pair
-  // (R <= 4). Lane i already holds the scales of pair i.
-  const int pi = lane < R ? lane : 0;
-  auto slot_lane = [](int i) { return (i & 1) * 32 + ((i >> 1) & 1) * 16; };  // 0, 32, 16, 48
-  const float g = __shfl(red[0], slot_lane(pi), kWave);
-  const float u = __shfl(red[R / 4], slot_lane(R + pi), kWave);
-  const float hv = silu(g * (sg * kCodeUnitInv)) * (u * (su * kCodeUnitInv));
-  if (lane < R && r0 + lane < d_ff) h[r0 + lane] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
+  // wave_reduce4 leaves operands 0..3 in lanes 0, 32, 16, 48: the gate sums
+  // of pairs 2q and 2q + 1 in lanes 0 and 16, their up sums in lanes 32 and
+  // 48. One lane swap brings those to lanes 0 and 16 of a second register,
+  // and lanes 0 and 16 form and store h of the two pairs.
+#pragma unroll
+  for (int q = 0; q < kRed; ++q) {
+    const auto gu = __builtin_amdgcn_permlane32_swap(as_u32(red[q]), as_u32(red[q]), false, false);
+    const float g = red[q], u = as_f32(gu[1]);
+    const float hv = silu(g * (sg[q] * kCodeUnitInv)) * (u * (su[q] * kCodeUnitInv));
+    const int pair = 2 * q + half;
+    if ((lane & 47) == 0 && pair < R && r0 + pair < d_ff)
+      h[r0 + pair] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
+  }
 }
 
 template <int SK, int T, int UPW, int MP>
