@@ -504,24 +504,32 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
   }
   const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
   if (fast && units <= 48) {
-    // Launch shapes from graph-timed sweeps on MI355X at M = 2..8. More tiles
-    // per workgroup (each activation column reused by more rows) beat more
-    // waves down to about 192-256 workgroups. n = 12,288: 3 tiles (5.6-6.2
-    // us); the q|k|v pack, n = 6,144: 2 tiles (4.4-4.9 us), at m = 2 one
-    // tile and 16 waves (4.3 us); n = 4,096: one tile, 16 waves at m = 3, 4
-    // (3.7 us) and 8 otherwise (3.4 us at m = 2, 3.9 at m = 8); K = 8,192
-    // and 12,288: 8 waves (4.4-5.5 and 6.0-7.6 us; 4 waves 5.0-6.0 and
-    // 6.6-8.0).
+    // Launch shapes from graph-timed sweeps on MI355X at M = 2..8, clocks
+    // settled, each shape timed in both orders. More tiles per workgroup
+    // (each activation column reused by more rows) beat more waves down to
+    // about 192-256 workgroups. n = 12,288: 3 tiles, 16 waves at m = 3, 4
+    // (5.37 us; 4 waves 5.57-5.59) and 4 otherwise (5.33 us at m = 2, 5.94 at
+    // m = 8); the q|k|v pack, n = 6,144: 2 tiles (4.45 us at m = 4), one tile
+    // of 16 waves at m = 2 (4.25 us); n < 5,120: one tile, 8 waves (q 3.39 /
+    // 3.55 / 3.52 / 3.96 us at m = 2 / 3 / 4 / 8; 16 waves 3.48-3.73); K =
+    // 8,192: 8 waves (4.69 / 5.50 us at m = 4 / 8); K = 12,288: 8 waves up to
+    // m = 4 (5.33 / 6.08 us at m = 2 / 4), 12 beyond (7.36 us at m = 8).
     if (units <= 16) {
-      if (n >= 8192) launch_mfma_cfg<4, 3, 4>(packed, scale, n, k, x, m, y, stream);
+      if (n >= 8192 && m == 2) launch_mfma_mp<4, 3, 4, 2>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 8192 && m <= 4) launch_mfma_mp<16, 3, 1, 4>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 8192) launch_mfma_mp<4, 3, 4, 8>(packed, scale, n, k, x, m, y, stream);
       else if (n >= 5120 && m == 2) launch_mfma_mp<16, 1, 1, 2>(packed, scale, n, k, x, m, y, stream);
-      else if (n >= 5120) launch_mfma_cfg<4, 2, 4>(packed, scale, n, k, x, m, y, stream);
-      else if (m == 3 || m == 4) launch_mfma_mp<16, 1, 1, 4>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 5120 && m <= 4) launch_mfma_mp<4, 2, 4, 4>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 5120) launch_mfma_mp<4, 2, 4, 8>(packed, scale, n, k, x, m, y, stream);
       else launch_mfma_cfg<8, 1, 2>(packed, scale, n, k, x, m, y, stream);
     } else if (units <= 32) {
       launch_mfma_cfg<8, 1, 4>(packed, scale, n, k, x, m, y, stream);
+    } else if (m == 2) {
+      launch_mfma_mp<8, 1, 6, 2>(packed, scale, n, k, x, m, y, stream);
+    } else if (m <= 4) {
+      launch_mfma_mp<8, 1, 6, 4>(packed, scale, n, k, x, m, y, stream);
     } else {
-      launch_mfma_cfg<8, 1, 6>(packed, scale, n, k, x, m, y, stream);
+      launch_mfma_mp<12, 1, 4, 8>(packed, scale, n, k, x, m, y, stream);
     }
     return hipGetLastError();
   }
