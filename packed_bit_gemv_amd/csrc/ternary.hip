@@ -282,8 +282,8 @@ __global__ __launch_bounds__(kGemvWaves* kWave) void ternary_gemm_small_kernel(c
 
 // Small M on the matrix cores (2 <= M <= 8, k % 8 == 0, x 16-byte aligned).
 // v_mfma_f32_16x16x32_f16 multiplies a 16-row tile of decoded codes (A,
-// 16 x 32) by up to 16 activation columns (B, 32 x 16; columns j >= M are
-// zero), so the cost per code does not grow with M. A lane with row i = lane
+// 16 x 32) by 16 activation columns (B, 32 x 16, of which columns j < M are
+// used), so the cost per code does not grow with M. A lane with row i = lane
 // % 16 and K-group g = lane / 16 loads 16 bytes (64 codes) of its row per
 // 256-column unit u: codes 256u + 64g .. +63. MFMA step v (0..7) of the unit
 // takes codes 256u + 64g + 8v .. +7 of that lane (word v/2, half v%2, decoded
