@@ -435,7 +435,11 @@ def main():
             lb = sum(ternary_bytes(*synth.SHAPES[p], m) for p in synth.PROJECTIONS)
             extra[f"layer_fused_m{m}_us"] = round(ms * 1e3, 3)
             extra[f"layer_fused_m{m}_GBs"] = round(lb / (ms * 1e-3) / 1e9, 1)
-            del graphs
+            g = capture(torch, lambda m=m: [fused_layer_m(l, m) for l in range(L)])
+            ms = time_graphs(torch, [g], 5, 1) / L
+            extra[f"layer_fused_m{m}_us_36_per_graph"] = round(ms * 1e3, 3)
+            extra[f"layer_fused_m{m}_GBs_36_per_graph"] = round(lb / (ms * 1e-3) / 1e9, 1)
+            del graphs, g
 
         # one speculative verify step: 36 fused layers and the greedy token of
         # each of the 8 rows through the head, one graph
