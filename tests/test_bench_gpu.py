@@ -1,0 +1,41 @@
+"""The benchmark's output line on a GPU: one JSON object with the fields and
+units its readers rely on, from a short run (few steps, small CPU budget)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.gpu
+def test_bench_json_line():
+    print("bench json line", flush=True)
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "20", "--warmup", "200",
+                           "--no-extra", "--cpu-budget", "1.5"], capture_output=True, text=True, timeout=600,
+                          cwd=ROOT)
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    lines = [l for l in proc.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, proc.stdout
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 200
+    assert d["unit"] == "GB/s" and d["higher_is_better"] is True and d["data"] == "synthetic"
+    assert d["vs_baseline"] is None
+    assert d["config"]["workload"] == "ffn_gate_up_down_m1"
+    assert d["value"] > 0 and d["ms_per_step"] > 0
+    # value is the step's algorithmic bytes over its time
+    step_bytes = 12_689_408 * 2 + 12_640_256
+    assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert 0 < r["achieved"] < r["peak"]
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    assert r["traffic"] is None or r["traffic"] > 25_296_896
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0 and c["cores"] >= 1
+    assert isinstance(c["sample"], str) and c["sample"]
