@@ -221,6 +221,32 @@ def test_small_m_exact_probe(pbg, m, n, k):
     assert np.array_equal(y, ref)
 
 
+def _random_shapes(seed: int, count: int):
+    """Seeded (n, k, m) over the dispatch's ranges: n up to 12,500, k up to
+    12,800 (multiples of 8 mostly, some not), n * k below 8 million."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < count:
+        n = int(rng.integers(1, 12_500))
+        k = int(rng.integers(1, 1_600)) * 8 + (int(rng.integers(1, 8)) if rng.random() < 0.15 else 0)
+        if n * k < 8_000_000:
+            out.append((n, k, int(rng.integers(1, 9))))
+    return out
+
+
+@pytest.mark.parametrize("n,k,m", _random_shapes(20261203, 24))
+def test_small_m_random_shapes_exact(pbg, n, k, m):
+    """Random shapes across every launch shape and kernel of the dispatch, exact probes."""
+    say(f"small-m random m={m} n={n} k={k}")
+    codes = synth.ternary_codes(9500 + n + k, n, k)
+    x = synth.probe_activations(9600 + m, m, k)
+    s = synth.pow2_scales(9700 + n, n)
+    ref = oracle.ternary_gemm_small(oracle.pack(codes)[0], s, k, x)
+    p, _, _ = gpu_pack(pbg, codes)
+    y = pbg.ternary_gemm_small(p, dev(s), k, dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, ref)
+
+
 @pytest.mark.parametrize("m", [2, 4, 7, 8])
 @pytest.mark.parametrize("proj", ["k", "o", "gate", "down"])
 def test_small_m_config_shapes(pbg, m, proj):
