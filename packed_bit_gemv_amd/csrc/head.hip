@@ -552,6 +552,11 @@ void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, 
   const int64_t units = (k / 16 + 3) / 4;  // 64-column units
   if (aligned && M == 1) {
     launch_head_fast<1, 4, 2, 8, AM>(w, scale, n, k, x, y, keys, stream);
+  } else if (aligned && M == 2) {
+    // two activation rows still fit the VALU path: 101.9 us against 106.8 us
+    // for the persistent matrix-core kernel on the 151,936 x 4,096 head (from
+    // M = 3 the VALU path loses, 128 against 108 us)
+    launch_head_fast<2, 4, 2, 4, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && k % kPKStep == 0 && k <= kPMaxK) {
     launch_head_persist<M, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M >= 3 && units <= 8 * 16) {
