@@ -303,6 +303,18 @@ def main():
         g = capture(torch, lambda p=p: [linear(l, p) for l in range(L)])
         per_proj_us[p] = time_graphs(torch, [g], 5, 1) * 1e3 / L
 
+    # streaming-read ceiling (pbg_stream_read: the GEMVs' loads, no decode),
+    # timed like the launches above: over the pool's packed gate matrices, and
+    # over L buffers of the gate|up launch's packed bytes
+    sink = torch.zeros(pbg.binding.STREAM_READ_SINK_WORDS, dtype=torch.int32, device=device)
+    g = capture(torch, lambda: [pbg.stream_read(model.layers[l]["gate"][0], sink) for l in range(L)])
+    read_gate_us = time_graphs(torch, [g], 5, 1) * 1e3 / L
+    gu_words = 2 * synth.words_bytes(*synth.SHAPES["gate"]) // 4
+    gu_pool = [torch.empty(gu_words, dtype=torch.int32, device=device) for _ in range(L)]
+    g = capture(torch, lambda: [pbg.stream_read(gu_pool[l], sink) for l in range(L)])
+    read_gu_us = time_graphs(torch, [g], max(5, args.steps // 40), 1) * 1e3 / L
+    del g, gu_pool
+
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
         with open(PROFILE_TRAFFIC) as f:
@@ -316,7 +328,8 @@ def main():
              "us_per_launch": {p: round(v, 3) for p, v in per_proj_us.items()},
              "GBs_per_launch": {p: round(ternary_bytes(*synth.SHAPES[p]) / (v * 1e-6) / 1e9, 1)
                                 for p, v in per_proj_us.items()},
-             "layers_in_pool": L, "pool_bytes_packed": bytes_step * L}
+             "layers_in_pool": L, "pool_bytes_packed": bytes_step * L,
+             "stream_read_us": {"gate_12.6MB": round(read_gate_us, 3), "gate_up_25.2MB": round(read_gu_us, 3)}}
 
     if not args.no_extra:
         K, W = max(20, args.steps // 4), 5
@@ -353,6 +366,10 @@ def main():
             ms = time_graphs(torch, [g], 4, 1) / HL
             extra[f"head_m{m}_us"] = round(ms * 1e3, 2)
             extra[f"head_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
+
+        g = capture(torch, lambda: [pbg.stream_read(hw, sink) for _ in range(HL)])
+        extra["stream_read_us"]["head_622MB"] = round(time_graphs(torch, [g], 4, 1) / HL * 1e3, 2)
+        del g
 
         def decode_step():
             for l in range(L):
@@ -510,6 +527,10 @@ def main():
             "kernel": "swiglu_gate_up_kernel",
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gate_up_us, 3),
+            "read_ceiling_us": round(read_gu_us, 3),
+            "frac_of_read_ceiling": round(read_gu_us / gate_up_us, 4),
+            "read_ceiling_note": "pbg_stream_read of the launch's packed bytes (25,165,824 B): the GEMVs' loads "
+                                 "alone, one launch each, timed the same way",
             "launch_us_note": f"HIP events around a replayed graph of {L} consecutive launches over the pool, "
                               f"divided by {L} (inter-launch gaps included)",
         },

@@ -242,6 +242,29 @@ int ternary_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scal
                              int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m, uint16_t* h, float* y,
                              hipStream_t stream);
 
+/*
+ * pbg_stream_read - measurement helper, not a step of the decode path: reads
+ * `bytes` of device memory once with the loads the GEMV kernels use (16-byte
+ * non-temporal loads, 1 KiB of consecutive bytes per wave-wide load, 4 in
+ * flight per lane) and only folds them by XOR. Its duration is the streaming-
+ * read ceiling for one launch that moves the same bytes, the reference a
+ * GEMV's time is set against.
+ * Source: Neutrino-1 8B model page, introduction (single-stream decode speed
+ * is set by the bytes moved per token).
+ *
+ *   src    device, 16-byte aligned; 16 <= bytes <= PBG_STREAM_READ_MAX_BYTES,
+ *          bytes % 16 == 0
+ *   sink   [PBG_STREAM_READ_SINK_WORDS] uint32 device, 4-byte aligned: the
+ *          call XORs into it, so with sink all zero before the call, the XOR
+ *          of all its words afterwards is the XOR of all 32-bit words of src
+ *          (every byte was read). Calls that overlap in time on one sink
+ *          still give the XOR of both ranges.
+ */
+#define PBG_STREAM_READ_SINK_WORDS 8192
+#define PBG_STREAM_READ_MAX_BYTES (1LL << 40)
+
+int pbg_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     int8_head_gemv,
     lib,
     pack_ternary,
+    stream_read,
     ternary_ffn_swiglu,
     ternary_swiglu_gate_up,
     ternary_gemm_small,
@@ -25,6 +26,7 @@ __all__ = [
     "int8_head_gemv",
     "lib",
     "pack_ternary",
+    "stream_read",
     "ternary_ffn_swiglu",
     "ternary_swiglu_gate_up",
     "ternary_gemm_small",

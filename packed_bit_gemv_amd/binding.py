@@ -18,6 +18,7 @@ from .build import LIB_PATH
 PBG_ERR_CODE = -4
 ARGMAX_KEYS_PER_ROW = 4096  # PBG_ARGMAX_KEYS_PER_ROW
 MAX_M = 8  # PBG_MAX_M
+STREAM_READ_SINK_WORDS = 8192  # PBG_STREAM_READ_SINK_WORDS
 
 _c_int = ctypes.c_int
 _c_i64 = ctypes.c_int64
@@ -39,6 +40,7 @@ _SIGNATURES = {
     "ternary_swiglu_gate_up_small": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "ternary_ffn_swiglu_small": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp,
                                           _vp]),
+    "pbg_stream_read": (_c_int, [_vp, _c_i64, _vp, _vp]),
 }
 
 
@@ -338,3 +340,24 @@ def ternary_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.T
                                             d_ff, x.data_ptr(), m, h.data_ptr(), y.data_ptr(), _stream(gate))
         _check("ternary_ffn_swiglu_small", rc)
     return h, y
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Read every byte of src once with the GEMVs' loads and fold them by XOR into sink.
+
+    A measurement helper: its time is the streaming-read ceiling for one launch
+    moving src.nbytes. sink is int32 [STREAM_READ_SINK_WORDS] (a new zeroed one
+    if None); afterwards the XOR of its words, XOR-ed with its XOR before the
+    call, is the XOR of all 32-bit words of src.
+    """
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous CUDA (HIP) tensor")
+    if sink is None:
+        sink = torch.zeros((STREAM_READ_SINK_WORDS,), dtype=torch.int32, device=src.device)
+    _dev(sink, "sink", torch.int32)
+    if tuple(sink.shape) != (STREAM_READ_SINK_WORDS,):
+        raise ValueError(f"sink must be [{STREAM_READ_SINK_WORDS}]")
+    nbytes = src.numel() * src.element_size()
+    rc = lib().pbg_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src))
+    _check("pbg_stream_read", rc)
+    return sink

@@ -11,6 +11,10 @@ bool bad_nk(int64_t n, int64_t k) { return n < 1 || n > PBG_MAX_N || k < 1 || k 
 
 bool bad_m(int64_t m) { return m < 1 || m > PBG_MAX_M; }
 
+bool bad_ffn(int64_t d_model, int64_t d_ff) {
+  return d_model < 8 || d_model > PBG_FFN_MAX_MODEL || d_model % 8 != 0 || bad_nk(d_ff, d_model);
+}
+
 int finish(hipError_t launch_status) {
   if (launch_status != hipSuccess) return PBG_ERR_HIP;
   return hipGetLastError() == hipSuccess ? PBG_OK : PBG_ERR_HIP;
@@ -98,11 +102,13 @@ int int8_embedding_gather(const int8_t* table, const float* scale, int64_t n, in
   return finish(pbg::launch_embedding_gather(table, scale, n, k, tokens, m, out, stream));
 }
 
-namespace {
-bool bad_ffn(int64_t d_model, int64_t d_ff) {
-  return d_model < 8 || d_model > PBG_FFN_MAX_MODEL || d_model % 8 != 0 || bad_nk(d_ff, d_model);
+int pbg_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return PBG_ERR_NULL;
+  if (bytes < 16 || bytes > PBG_STREAM_READ_MAX_BYTES || bytes % 16 != 0) return PBG_ERR_SHAPE;
+  if (misaligned(src, 16) || misaligned(sink, 4)) return PBG_ERR_ALIGN;
+  (void)hipGetLastError();
+  return finish(pbg::launch_stream_read(src, bytes, sink, stream));
 }
-}  // namespace
 
 int ternary_swiglu_gate_up(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
                            const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
@@ -130,7 +136,6 @@ int ternary_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, con
   return finish(pbg::launch_ffn_swiglu(gate_packed, gate_scale, up_packed, up_scale, down_packed, down_scale, d_model,
                                        d_ff, x, h, y, stream));
 }
-
 
 int ternary_swiglu_gate_up_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
                                  const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m,

@@ -42,6 +42,9 @@ hipError_t launch_ffn_swiglu_small(const uint32_t* gate, const float* gate_scale
                                    int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* y,
                                    hipStream_t stream);
 
+// One read of `bytes` (a multiple of 16) from 16-byte aligned src, folded into sink.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Workgroups one embedding gather launches (the grid must stay below 2^31 / 256).
 int64_t embedding_blocks(int64_t m, int64_t k);
 

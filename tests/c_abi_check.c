@@ -67,6 +67,9 @@ int main(void) {
   expect("ffn small null y",
          ternary_ffn_swiglu_small(packed, scale, packed, scale, packed, scale, 4096, 64, x, 4, h, NULL, 0),
          PBG_ERR_NULL);
+  expect("stream read bytes not a multiple of 16", pbg_stream_read(w, 1000, (uint32_t*)(base + 0x8000), 0),
+         PBG_ERR_SHAPE);
+  expect("stream read src misaligned", pbg_stream_read(w + 8, 1024, (uint32_t*)(base + 0x8000), 0), PBG_ERR_ALIGN);
   if (failures == 0) printf("ok\n");
   return failures == 0 ? 0 : 1;
 }

@@ -149,3 +149,13 @@ def test_ffn_small_validation():
     assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, 4, GOOD, GOOD + 2, None) == -3   # y
     assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, 4, None, None) == -1
     assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD + 4, GOOD, 4096, 12288, GOOD, 4, GOOD, None) == -3
+
+
+def test_stream_read_validation():
+    lib = binding.lib()
+    assert lib.pbg_stream_read(None, 1024, GOOD, None) == -1
+    assert lib.pbg_stream_read(GOOD, 1024, None, None) == -1
+    for nbytes in (0, 8, 1000, -16, 2 ** 40 + 16):
+        assert lib.pbg_stream_read(GOOD, nbytes, GOOD, None) == -2
+    assert lib.pbg_stream_read(GOOD + 8, 1024, GOOD, None) == -3
+    assert lib.pbg_stream_read(GOOD, 1024, GOOD + 2, None) == -3

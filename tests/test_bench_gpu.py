@@ -36,6 +36,9 @@ def test_bench_json_line():
     assert 0 < r["achieved"] < r["peak"]
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert r["traffic"] is None or r["traffic"] > 25_296_896
+    # the loads alone of the same packed bytes, one launch each
+    assert 0 < r["read_ceiling_us"] and 0 < r["frac_of_read_ceiling"] < 1.5
+    assert d["extra"]["stream_read_us"]["gate_12.6MB"] > 0
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0 and c["cores"] >= 1
     assert isinstance(c["sample"], str) and c["sample"]
