@@ -403,6 +403,21 @@ def main():
             extra[f"head_argmax_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
             del g
 
+        # the embedding row of each token (int8 row x row scale, 4 KiB read per
+        # token); the head tensor stands in for the input embedding, which has
+        # the same shape and type
+        for m in (1, 8):
+            ids = np.random.default_rng(synth.SEED_HEAD + m).integers(0, hn, m).astype(np.int32)
+            toks = torch.from_numpy(ids).to(device)
+            emb = torch.empty((m, hk), dtype=torch.float32, device=device)
+            g = capture(torch, lambda toks=toks, emb=emb: [pbg.int8_embedding_gather(hw, hs, toks, emb)
+                                                           for _ in range(36)])
+            ms = time_graphs(torch, [g], 5, 1) / 36
+            eb = m * (hk + 4 + 4 + 4 * hk)  # row, scale and id in; fp32 row out
+            extra[f"embedding_m{m}_us"] = round(ms * 1e3, 3)
+            extra[f"embedding_m{m}_GBs"] = round(eb / (ms * 1e-3) / 1e9, 1)
+            del g, toks, emb
+
         # shared-input fusions: q|k|v as one packed matrix (row concatenation of
         # packs with the same K is itself a pack), o, then the FFN block
         fused = []
