@@ -403,6 +403,21 @@ def main():
             extra[f"head_argmax_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
             del g
 
+        # pack_ternary (load time, not per token): the gate shape over a pool of 8
+        # code tensors (403 MB of int8 codes, above the Infinity Cache)
+        n, k = synth.SHAPES["gate"]
+        codes_pool = [synth.ternary_codes_device(synth.tensor_seed(l, "gate"), n, k, synth.code_dist(l, "gate"),
+                                                 device) for l in range(8)]
+        pk = torch.empty((n, pbg.words_per_row(k)), dtype=torch.int32, device=device)
+        rs = torch.empty(n, dtype=torch.int32, device=device)
+        stt = torch.empty(4, dtype=torch.int64, device=device)
+        g = capture(torch, lambda: [pbg.pack_ternary(c, pk, rs, stt, check=False) for c in codes_pool])
+        ms = time_graphs(torch, [g], 5, 1) / len(codes_pool)
+        pb = n * k + synth.words_bytes(n, k) + 4 * n + 32  # codes in; words, row sums and counts out
+        extra["pack_gate_us"] = round(ms * 1e3, 2)
+        extra["pack_gate_GBs"] = round(pb / (ms * 1e-3) / 1e9, 1)
+        del g, codes_pool, pk, rs, stt
+
         # the embedding row of each token (int8 row x row scale, 4 KiB read per
         # token); the head tensor stands in for the input embedding, which has
         # the same shape and type

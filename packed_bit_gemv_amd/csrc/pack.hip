@@ -8,31 +8,48 @@
 namespace pbg {
 namespace {
 
-constexpr int kPackWaves = 4;         // waves per workgroup
-constexpr int kPackMaxBlocks = 4096;  // the grid stays far below the launch limits at any n
+// At most 256 workgroups of 16 waves: each workgroup ends with one 64-bit
+// atomic per nonzero code count, and atomics on the four counts (one cache
+// line) serialise at the memory side, so the grid is kept small; 16 waves per
+// CU still keep 64 KiB of codes in flight.
+constexpr int kPackWaves = 16;        // waves per workgroup
+constexpr int kPackMaxBlocks = 256;
+constexpr int kPackBatch = 4;         // words per lane whose loads are in flight together
 
-// Nonzero and sign bit of code j (0..15) in its word.
+// Nonzero bit of code j (0..15) in its word; the sign bit is the next one up.
 __device__ __forceinline__ uint32_t nz_bit(int j) { return 16u * (j & 1) + 14u - 2u * (j >> 1); }
-__device__ __forceinline__ uint32_t sign_bit(int j) { return nz_bit(j) + 1u; }
 
 struct Tally {
   int minus, zero, plus, invalid;
 };
 
-__device__ __forceinline__ void put_code(int c, int j, uint32_t& word, int& sum, Tally& t) {
-  if (c == 1) {
-    word |= 1u << nz_bit(j);
-    sum += 1;
-    t.plus += 1;
-  } else if (c == -1) {
-    word |= (1u << nz_bit(j)) | (1u << sign_bit(j));
-    sum -= 1;
-    t.minus += 1;
-  } else if (c == 0) {
-    t.zero += 1;
-  } else {
-    t.invalid += 1;
-  }
+// Field of one code byte: a valid code (0x00, 0x01 or 0xFF as a byte) is its
+// own 2-bit two's complement, b & 3; anything else packs as 0 and is counted.
+__device__ __forceinline__ void put_code(uint32_t b, int j, uint32_t& word, int& bad) {
+  const bool ok = ((b + 1u) & 0xFFu) <= 2u;
+  bad += ok ? 0 : 1;
+  word |= (ok ? (b & 3u) : 0u) << nz_bit(j);
+}
+
+// Packs the 16 code bytes of v into one word.
+__device__ __forceinline__ uint32_t pack16(const uint4& v, int& bad) {
+  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) put_code((q[j >> 2] >> (8 * (j & 3))) & 0xFFu, j, word, bad);
+  return word;
+}
+
+// Counts of a packed word holding `codes` codes, `bad` of them invalid (and
+// packed as 0): its nonzero bits mark +1 and -1, its sign bits -1.
+__device__ __forceinline__ void tally(uint32_t word, int codes, int bad, int& sum, Tally& t) {
+  const int nz = __popc(word & 0x55555555u);
+  const int minus = __popc(word & 0xAAAAAAAAu);
+  t.plus += nz - minus;
+  t.minus += minus;
+  t.zero += codes - bad - nz;
+  t.invalid += bad;
+  sum += nz - 2 * minus;
 }
 
 __global__ void zero_stats_kernel(int64_t* stats) {
@@ -40,10 +57,11 @@ __global__ void zero_stats_kernel(int64_t* stats) {
 }
 
 // One wave per row at a time (rows wave, wave + all waves, ...); lane l packs
-// words l, l + 64, ... of the row. The row sum is reduced across the wave;
-// the code counts are kept per lane over all rows of the wave, reduced per
-// workgroup and added to the totals with one 64-bit atomic each (integers:
-// the order of additions does not matter).
+// words l, l + 64, ... of the row, with the loads of kPackBatch words in
+// flight together when the row is whole 16-byte chunks. The row sum is
+// reduced across the wave; the code counts are kept per lane over all rows of
+// the wave, reduced per workgroup and added to the totals with one 64-bit
+// atomic each (integers: the order of additions does not matter).
 __global__ __launch_bounds__(kPackWaves* kWave) void pack_kernel(const int8_t* __restrict__ codes, int64_t n,
                                                                  int64_t k, int64_t words,
                                                                  uint32_t* __restrict__ packed,
@@ -56,21 +74,38 @@ __global__ __launch_bounds__(kPackWaves* kWave) void pack_kernel(const int8_t* _
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kPackWaves;
   for (int64_t row = static_cast<int64_t>(blockIdx.x) * kPackWaves + wave; row < n; row += stride) {
     const int8_t* src = codes + row * k;
+    uint32_t* dst = packed + row * words;
     int sum = 0;
-    for (int64_t w = lane; w < words; w += kWave) {
-      uint32_t word = 0;
-      const int64_t c0 = 16 * w;
-      if (c0 < k) {
-        if (vec) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src + c0);
-          const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    if (vec) {
+      const int64_t full = k / 16;  // words that hold codes; the rest is padding
+      for (int64_t w0 = 0; w0 < words; w0 += kWave * kPackBatch) {
+        uint4 v[kPackBatch];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) put_code(static_cast<int8_t>(q[j >> 2] >> (8 * (j & 3))), j, word, sum, t);
-        } else {
-          for (int j = 0; j < 16 && c0 + j < k; ++j) put_code(src[c0 + j], j, word, sum, t);
+        for (int u = 0; u < kPackBatch; ++u) {
+          const int64_t w = w0 + lane + u * kWave;
+          v[u] = w < full ? *reinterpret_cast<const uint4*>(src + 16 * w) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kPackBatch; ++u) {
+          const int64_t w = w0 + lane + u * kWave;
+          if (w < words) {
+            int bad = 0;
+            const uint32_t word = pack16(v[u], bad);
+            if (w < full) tally(word, 16, bad, sum, t);
+            dst[w] = word;
+          }
         }
       }
-      packed[row * words + w] = word;
+    } else {
+      for (int64_t w = lane; w < words; w += kWave) {
+        const int64_t c0 = 16 * w;
+        const int codes_here = c0 < k ? static_cast<int>(k - c0 < 16 ? k - c0 : 16) : 0;
+        uint32_t word = 0;
+        int bad = 0;
+        for (int j = 0; j < codes_here; ++j) put_code(static_cast<uint8_t>(src[c0 + j]), j, word, bad);
+        tally(word, codes_here, bad, sum, t);
+        dst[w] = word;
+      }
     }
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
