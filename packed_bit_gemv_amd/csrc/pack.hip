@@ -31,13 +31,30 @@ __device__ __forceinline__ void put_code(uint32_t b, int j, uint32_t& word, int&
   word |= (ok ? (b & 3u) : 0u) << nz_bit(j);
 }
 
+// The fields of code bytes 4q .. 4q + 3 (bytes 0..3 of u) at their places in
+// the word, four bytes at a time:
+//  - t = b + 1 (mod 256) per byte, without carries between bytes; a valid code
+//    gives t <= 2;
+//  - bit 7 of a byte of `inv` is set when t >= 3, an invalid code;
+//  - f holds b & 3 of every valid byte and 0 for the invalid ones;
+//  - a byte permute puts codes 4q + 2 and 4q (the low half's two fields) 8 bits
+//    apart in the low half and codes 4q + 3 and 4q + 1 in the high half, and a
+//    shift by 6 closes each gap, leaving the fields of pair 2q + 1 below those
+//    of pair 2q; the final shift moves pair 2q to bits 14 - 4q (low half) and
+//    30 - 4q (high half).
+__device__ __forceinline__ uint32_t pack4(uint32_t u, int q, int& bad) {
+  const uint32_t t = ((u & 0x7F7F7F7Fu) + 0x01010101u) ^ (u & 0x80808080u);
+  const uint32_t inv = (((t & 0x7F7F7F7Fu) + 0x7D7D7D7Du) | t) & 0x80808080u;
+  bad += __popc(inv);
+  const uint32_t f = u & 0x03030303u & ~((inv >> 6) | (inv >> 7));
+  const uint32_t g = __builtin_amdgcn_perm(f, f, 0x01030002u);  // bytes (2, 0, 3, 1) of f
+  const uint32_t h = (g | (g >> 6)) & 0x000F000Fu;
+  return h << (12 - 4 * q);
+}
+
 // Packs the 16 code bytes of v into one word.
 __device__ __forceinline__ uint32_t pack16(const uint4& v, int& bad) {
-  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-  uint32_t word = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) put_code((q[j >> 2] >> (8 * (j & 3))) & 0xFFu, j, word, bad);
-  return word;
+  return pack4(v.x, 0, bad) | pack4(v.y, 1, bad) | pack4(v.z, 2, bad) | pack4(v.w, 3, bad);
 }
 
 // Counts of a packed word holding `codes` codes, `bad` of them invalid (and
