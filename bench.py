@@ -340,6 +340,11 @@ def main():
             n, k = synth.SHAPES[p]
             extra["us_per_launch"][p] = round(us, 3)
             extra["GBs_per_launch"][p] = round(ternary_bytes(n, k) / (us * 1e-6) / 1e9, 1)
+        # read ceiling of the smaller packed shapes: q/o 4.2 MB, k/v 1.0 MB
+        for p, label in (("q", "q_4.2MB"), ("k", "k_1.0MB")):
+            g = capture(torch, lambda p=p: [pbg.stream_read(model.layers[l][p][0], sink) for l in range(L)])
+            extra["stream_read_us"][label] = round(time_graphs(torch, [g], 5, 1) * 1e3 / L, 3)
+            del g
 
         def layer_step(layer, m=1):
             for p in synth.PROJECTIONS:

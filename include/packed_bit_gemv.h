@@ -245,8 +245,8 @@ int ternary_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scal
 /*
  * pbg_stream_read - measurement helper, not a step of the decode path: reads
  * `bytes` of device memory once with the loads the GEMV kernels use (16-byte
- * non-temporal loads, 1 KiB of consecutive bytes per wave-wide load, 4 in
- * flight per lane) and only folds them by XOR. Its duration is the streaming-
+ * non-temporal loads, 1 KiB of consecutive bytes per wave-wide load, up to
+ * 4 in flight per lane) and only folds them by XOR. Its duration is the streaming-
  * read ceiling for one launch that moves the same bytes, the reference a
  * GEMV's time is set against.
  * Source: Neutrino-1 8B model page, introduction (single-stream decode speed

@@ -33,11 +33,12 @@ def fold(sink) -> int:
     return int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
 
 
-# one chunk, one 256-thread workgroup less a chunk / exactly / plus a chunk, a
-# ragged multi-workgroup size, the 12288 x 4096 packed matrix, and on the
-# 512-thread shape (from 16 MiB) its first size and a ragged 25 MB range
-@pytest.mark.parametrize("nbytes", [16, 16 * 1023, 16 * 1024, 16 * 1025, 16 * 300_001, 12_582_912, 16 << 20,
-                                    25_165_840])
+# below 8 MiB (one load per lane): one chunk, one workgroup less a chunk /
+# exactly / plus a chunk, a ragged multi-workgroup size; from 8 MiB (four loads
+# per lane): its first size, a ragged one and the 12288 x 4096 packed matrix;
+# from 16 MiB (512 threads): its first size and a ragged 25 MB range
+@pytest.mark.parametrize("nbytes", [16, 16 * 255, 16 * 256, 16 * 257, 16 * 300_001, 8 << 20, (8 << 20) + 16 * 1025,
+                                    12_582_912, 16 << 20, 25_165_840])
 def test_stream_read_folds_every_word(pbg, nbytes):
     say(f"stream_read bytes={nbytes}")
     words = np.random.default_rng(20261203 + nbytes).integers(0, 2 ** 32, nbytes // 4, dtype=np.uint64)
