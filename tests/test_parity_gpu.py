@@ -105,6 +105,32 @@ def test_pack_invalid_codes(pbg):
     assert st.cpu().numpy()[3] == 2
 
 
+@pytest.mark.parametrize("n,k", [(8, 320), (5, 4096), (3, 12288)])
+def test_pack_invalid_codes_whole_chunks(pbg, n, k):
+    """Rows of whole 16-byte chunks (four code bytes packed at a time) with every kind of invalid byte at
+    several places in a word: each packs as 0 and adds nothing to the row sum; the counts split exactly."""
+    say(f"pack invalid whole chunks n={n} k={k}")
+    codes = synth.ternary_codes(79 + k, n, k)
+    rng = np.random.default_rng(80 + k)
+    bad_vals = np.array([2, 3, 126, 127, -2, -3, -127, -128], dtype=np.int8)
+    cells = rng.choice(n * k, size=64, replace=False)
+    raw = codes.copy().reshape(-1)
+    raw[cells] = bad_vals[np.arange(64) % len(bad_vals)]
+    raw = raw.reshape(n, k)
+    valid = codes.copy().reshape(-1)
+    valid[cells] = 0
+    valid = valid.reshape(n, k)
+    p, rs, st = pbg.pack_ternary(dev(raw), check=False)
+    ref_p, ref_rs, _ = oracle.pack(valid)
+    assert np.array_equal(host_words(p), ref_p)
+    assert np.array_equal(rs.cpu().numpy(), ref_rs)
+    inval = np.zeros(n * k, dtype=bool)
+    inval[cells] = True
+    inval = inval.reshape(n, k)
+    expect = [int(((raw == -1) & ~inval).sum()), int(((raw == 0) & ~inval).sum()), int(((raw == 1) & ~inval).sum()), 64]
+    assert st.cpu().numpy().tolist() == expect
+
+
 # --------------------------------------------------------------------------
 # ternary_gemv (M = 1)
 # --------------------------------------------------------------------------
