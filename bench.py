@@ -368,12 +368,12 @@ def main():
         HL = 8
         for m in (1, 2, 4, 7, 8):
             g = capture(torch, lambda m=m: [head(m) for _ in range(HL)])
-            ms = time_graphs(torch, [g], 4, 1) / HL
+            ms = time_graphs(torch, [g], 8, 2) / HL
             extra[f"head_m{m}_us"] = round(ms * 1e3, 2)
             extra[f"head_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
 
         g = capture(torch, lambda: [pbg.stream_read(hw, sink) for _ in range(HL)])
-        extra["stream_read_us"]["head_622MB"] = round(time_graphs(torch, [g], 4, 1) / HL * 1e3, 2)
+        extra["stream_read_us"]["head_622MB"] = round(time_graphs(torch, [g], 8, 2) / HL * 1e3, 2)
         del g
 
         def decode_step():
@@ -400,10 +400,10 @@ def main():
         keys = torch.zeros(8 * pbg.binding.ARGMAX_KEYS_PER_ROW, dtype=torch.int64, device=device)
         tok = torch.empty(8, dtype=torch.int32, device=device)
         lgt = torch.empty(8, dtype=torch.float32, device=device)
-        for m in (1, 7):
+        for m in (1, 7, 8):
             g = capture(torch, lambda m=m: [pbg.int8_head_argmax(hw, hs, xs[hk][:m], keys, tok[:m], lgt[:m])
                                             for _ in range(HL)])
-            ms = time_graphs(torch, [g], 4, 1) / HL
+            ms = time_graphs(torch, [g], 8, 2) / HL
             extra[f"head_argmax_m{m}_us"] = round(ms * 1e3, 2)
             extra[f"head_argmax_m{m}_GBs"] = round(head_bytes(hn, hk, m) / (ms * 1e-3) / 1e9, 1)
             del g
