@@ -49,10 +49,17 @@ def ternary_bytes(n: int, k: int, m: int = 1) -> int:
     return synth.words_bytes(n, k) + 4 * n + 2 * m * k + 4 * m * n
 
 
-def gate_up_bytes(d_ff: int, d_model: int) -> int:
+def gate_up_bytes(d_ff: int, d_model: int, m: int = 1) -> int:
     """Algorithmic bytes of the gate|up + SwiGLU launch: both packed matrices,
-    both scale vectors, x once, h (fp16) out."""
-    return 2 * synth.words_bytes(d_ff, d_model) + 2 * 4 * d_ff + 2 * d_model + 2 * d_ff
+    both scale vectors, x in once, h (fp16) out."""
+    return 2 * synth.words_bytes(d_ff, d_model) + 2 * 4 * d_ff + 2 * m * d_model + 2 * m * d_ff
+
+
+def ffn_block_bytes(d_model: int, d_ff: int, m: int = 1) -> int:
+    """Algorithmic bytes of the fused block as it runs: the gate|up launch
+    plus the down GEMV on h (packed down, its scales, h in, y out). At
+    d_model 4,096, d_ff 12,288, m = 1: 25,296,896 + 12,640,256 = 37,937,152."""
+    return gate_up_bytes(d_ff, d_model, m) + ternary_bytes(d_model, d_ff, m)
 
 
 def head_bytes(n: int, k: int, m: int = 1) -> int:
@@ -127,15 +134,15 @@ def time_graphs(torch, graphs, steps: int, warmup: int):
 
 
 def cpu_baseline(budget_s: float):
-    """The CPU oracle timed on this host on a bounded sample of the workload."""
+    """The CPU oracle timed on this host on a bounded sample of the workload.
+
+    cores = the CPUs this process may run on (its affinity mask); the oracle's
+    BLAS matvec is limited to that many threads, its NumPy unpack runs on one.
+    The unpack is also timed alone, so that the matvec's share follows.
+    """
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
-    except Exception:
-        threads = 1
+    cores = len(os.sched_getaffinity(0))
     rows = 1024
     samples = []
     for p in ("gate", "up", "down"):
@@ -153,16 +160,27 @@ def cpu_baseline(budget_s: float):
             reps += 1
         return done, reps, time.perf_counter() - t0
 
-    done_bytes, reps, dt = run(budget_s, oracle.ternary_gemv)
-    # the unpack alone, and the whole oracle restricted to one BLAS thread
-    _, u_reps, u_dt = run(budget_s / 6, lambda packed, s, k, x: oracle.unpack(packed, k))
-    one = None
     try:
         from threadpoolctl import threadpool_limits
+    except Exception:  # without it BLAS keeps its own thread count
+        threadpool_limits = None
 
-        with threadpool_limits(limits=1):
-            b1, _, dt1 = run(budget_s / 3, oracle.ternary_gemv)
-        one = round(b1 / dt1 / 1e9, 4)
+    def limited(threads, seconds, fn):
+        if threadpool_limits is None:
+            return run(seconds, fn)
+        with threadpool_limits(limits=threads):
+            return run(seconds, fn)
+
+    done_bytes, reps, dt = limited(cores, budget_s, oracle.ternary_gemv)
+    _, u_reps, u_dt = run(budget_s / 6, lambda packed, s, k, x: oracle.unpack(packed, k))
+    b1, _, dt1 = limited(1, budget_s / 3, oracle.ternary_gemv)
+    blas_threads = cores
+    try:
+        from threadpoolctl import threadpool_info
+
+        with threadpool_limits(limits=cores):
+            blas_threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()
+                                      if i.get("user_api") == "blas"])
     except Exception:
         pass
     model = ""
@@ -171,15 +189,20 @@ def cpu_baseline(budget_s: float):
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
+    pass_s, unpack_s = dt / reps, u_dt / u_reps
     return {
         "value": round(done_bytes / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"{reps} passes over the first {rows} rows of layer-1 gate, up and down (M=1), "
-                   f"{dt:.1f} s; unpack in NumPy (1 thread) + fp64 matvec in BLAS ({threads} threads)"),
-        "unpack_share": round((u_dt / u_reps) / (dt / reps), 3),
-        "value_1_thread": one,
+                   f"{dt:.1f} s; unpack in NumPy (1 thread) + fp64 matvec in BLAS ({blas_threads} threads)"),
+        "blas_threads": blas_threads,
+        "pass_s": round(pass_s, 5),
+        "unpack_s": round(unpack_s, 5),
+        "matvec_s": round(pass_s - unpack_s, 5),
+        "unpack_share": round(unpack_s / pass_s, 3),
+        "value_1_thread": round(b1 / dt1 / 1e9, 4),
         "cpu_model": model,
     }
 
@@ -263,12 +286,16 @@ def main():
     W0, K0 = args.warmup, args.steps
     warm = capture(torch, lambda: [ffn_block(i % L) for i in range(W0)]) if W0 > 0 else None
     timed = capture(torch, lambda: [ffn_block((W0 + i) % L) for i in range(K0)])
-    bytes_step = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)
+    # the fused path's own bytes (h written once as fp16 and read back by down)
+    bytes_step = ffn_block_bytes(synth.HIDDEN, synth.FFN)
+    three_bytes = sum(ternary_bytes(*synth.SHAPES[p]) for p in ffn)  # as three separate GEMVs
     # Untimed, whatever W is: ~20 ms of the same steps first, so that the
     # chip's clocks have settled when the W warm-up and K timed steps run.
     settle = capture(torch, lambda: [ffn_block(i % L) for i in range(L)])
-    for _ in range(max(1, round(20e-3 / (L * 12e-6)))):
+    settle_replays = max(1, round(20e-3 / (L * 12e-6)))
+    for _ in range(settle_replays):
         settle.replay()
+    settle_steps = settle_replays * L
     del settle
     if warm is not None:
         warm.replay()
@@ -315,20 +342,24 @@ def main():
     read_gu_us = time_graphs(torch, [g], max(5, args.steps // 40), 1) * 1e3 / L
     del g, gu_pool
 
-    traffic = None
+    traffic, traffic_note = None, "null: the counter reading on file was taken from other kernel source"
     if os.path.exists(PROFILE_TRAFFIC):
         with open(PROFILE_TRAFFIC) as f:
             tr = json.load(f)
         if tr.get("kernel_hash") == kernel_hash():
             traffic = tr.get("bytes_per_launch")
+            traffic_note = ("stored, not measured in this run: rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, "
+                            "scaled by a plain copy's reading, from profiles/traffic_swiglu_gate_up_m1.json; "
+                            f"emitted only while the kernel source hash equals the stored one ({tr['kernel_hash']})")
 
     extra = {"ffn_three_gemv_m1_us": round(three_us, 3),
-             "ffn_three_gemv_m1_GBs": round(bytes_step / (three_us * 1e-6) / 1e9, 1),
+             "ffn_three_gemv_m1_GBs": round(three_bytes / (three_us * 1e-6) / 1e9, 1),
+             "ffn_three_gemv_m1_bytes": three_bytes,
              "swiglu_gate_up_us_per_launch": round(gate_up_us, 3),
              "us_per_launch": {p: round(v, 3) for p, v in per_proj_us.items()},
              "GBs_per_launch": {p: round(ternary_bytes(*synth.SHAPES[p]) / (v * 1e-6) / 1e9, 1)
                                 for p, v in per_proj_us.items()},
-             "layers_in_pool": L, "pool_bytes_packed": bytes_step * L,
+             "layers_in_pool": L, "pool_bytes_packed": 3 * synth.words_bytes(synth.FFN, synth.HIDDEN) * L,
              "stream_read_us": {"gate_12.6MB": round(read_gate_us, 3), "gate_up_25.2MB": round(read_gu_us, 3)}}
 
     if not args.no_extra:
@@ -538,6 +569,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -550,7 +582,12 @@ def main():
             "m": 1,
             "layers_in_pool": L,
             "us_per_step": round(ms_step * 1e3, 3),
+            "bytes_per_step": bytes_step,
             "path": "ternary_ffn_swiglu: gate|up + SwiGLU in one launch, then the down GEMV on its fp16 output",
+            "untimed": f"{settle_steps} settle steps (~20 ms, for the clocks) then the {args.warmup} warm-up steps",
+            "plain_three_gemv": {"us_per_step": round(three_us, 3),
+                                 "GBs": round(three_bytes / (three_us * 1e-6) / 1e9, 1),
+                                 "bytes_per_step": three_bytes},
         },
         "roofline": {
             "bound": "hbm",
@@ -559,6 +596,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_note": traffic_note,
             "kernel": "swiglu_gate_up_kernel",
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gate_up_us, 3),

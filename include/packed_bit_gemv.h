@@ -5,13 +5,15 @@
  *
  * What is computed (Neutrino-1 8B model page, English text on bittide):
  *   - every transformer linear is stored as ternary codes c in {-1, 0, +1}
- *     with a scale and a row sum per row; the kernels expand the codes while
- *     multiplying and never hold the weights as fp16/fp32 arrays (introduction; "Where the
- *     bytes live"; "Inside the coded lane");
+ *     with a scale and a row sum per row; the kernels read the packed codes
+ *     and decode them in registers, so no fp16/fp32 copy of a weight matrix
+ *     exists anywhere (introduction; "Where the bytes live"; "Inside the
+ *     coded lane");
  *   - the untied output head is an int8 tensor with a per-row scale
  *     ("Where the bytes live");
- *   - speculative verification checks a whole drafted run of tokens with one
- *     forward pass ("speculative" section), i.e. the same products for M <= 8 rows.
+ *   - a speculative verify step puts several drafted positions through the
+ *     same weights together ("speculative" section): the same products for
+ *     M <= 8 activation rows.
  *
  * Packed layout (this library's own; the page calls its format proprietary):
  *   - 2 bits per code, 16 codes per little-endian uint32 word;
@@ -37,9 +39,14 @@
  *     the call returns without waiting, except where stated;
  *   - arguments are validated before any HIP call; on a validation error
  *     nothing is enqueued and a negative PBG_ERR_* code is returned;
+ *   - a HIP error that earlier work left pending on the calling thread
+ *     (hipPeekAtLastError) belongs to the caller: the call enqueues nothing,
+ *     leaves that error in place and returns PBG_ERR_HIP (hipErrorNotReady,
+ *     a completion status, is not treated as an error);
  *   - outputs must not overlap inputs;
  *   - activations x are IEEE fp16 bit patterns (uint16_t), row-major [m][k];
- *     they must be finite: a zero code contributes 0 * x_j;
+ *     they must be finite (the result for Inf or NaN activations is not
+ *     specified; the kernels form 0 * x_j for a zero code);
  *   - outputs y are fp32, row-major [m][n]; accumulation is fp32 in an
  *     unspecified order (any order meets |y - y_exact| <= 1e-3 * s_r *
  *     sum_j |x_j| for K below about 16,000).
@@ -141,9 +148,10 @@ int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, co
  * int8_head_argmax - greedy token of each activation row through the int8
  * head without writing the logits: token[i] = argmax_v Y[i][v] with Y as in
  * int8_head_gemv, the lowest v among equal maxima; logit[i] = Y[i][token[i]].
- * Source: Neutrino-1 8B model page, "speculative" section (a drafted token
- * is accepted only when it equals the 8B's own argmax, so decoding stays the
- * plain greedy stream) and "Where the bytes live" (int8 head).
+ * Source: Neutrino-1 8B model page, "speculative" section (acceptance of a
+ * drafted token compares it with the large model's greedy choice, so the
+ * verify step needs only this index per row) and "Where the bytes live"
+ * (int8 head).
  *
  *   w, scale, x, m  as int8_head_gemv (1 <= m <= 8); logits must be finite
  *   keys    [m * PBG_ARGMAX_KEYS_PER_ROW] uint64 device workspace, 8-byte

@@ -17,11 +17,11 @@ What it computes (Neutrino-1 8B model page, English text on bittide):
 * A linear applied to one activation row x is y_r = s_r * sum_j c_rj * x_j.
 * The untied output head is an int8 tensor with a per-row scale
   ("Where the bytes live"): y_v = s_v * sum_j w_vj * x_j.
-* The speculative verify pass scores a whole drafted run in one forward pass
-  ("speculative" section), i.e. the same products for M activation rows, and a
-  drafted token is kept only when it equals the 8B's own argmax: the greedy
-  token of each row is the index of its largest head logit (lowest index
-  among equal maxima).
+* Speculative decoding ("speculative" section) checks a run of drafted
+  tokens with one pass of the large model, so the same products run on M
+  activation rows; acceptance compares each drafted token with the large
+  model's greedy choice, taken here as the index of the row's largest head
+  logit (the lowest index among equal maxima).
 * The int8 input embedding has a per-row scale and is read one row per token
   ("Where the bytes live"): the embedding of token t is s_t * w_t.
 * The feed-forward block is gated (SwiGLU) with three linears per layer
@@ -41,6 +41,10 @@ Bit layout of one 32-bit word (little-endian uint32) holding 16 codes:
 Row layout: row r holds W = 4 * ceil(K / 64) words; word w holds the codes of
 columns 16*w .. 16*w + 15; codes past column K - 1 are 0 (row padding, so a
 row is a whole number of 16-byte chunks).
+
+Activations must be finite (Inf and NaN raise ValueError): the product of a
+zero code and a non-finite activation is left undefined, as the library's
+header requires finite activations of its callers.
 
 Arithmetic: activations arrive as fp16 and are widened to fp64 exactly; codes
 and int8 weights are exact in fp64; the matrix-vector product is a float64
@@ -145,6 +149,13 @@ def unpack(packed: np.ndarray, k: int) -> np.ndarray:
 
 
 def _as_rows(x: np.ndarray, k: int) -> np.ndarray:
+    """fp16 activations [k] or [m, k] widened exactly to fp64 rows [m, k].
+
+    Activations must be finite: a product against them is defined only for
+    finite values here (a zero code against Inf would otherwise have to pick
+    between 0 and NaN, and the pages say nothing about it), so Inf or NaN is
+    rejected with ValueError rather than given a meaning.
+    """
     x = np.asarray(x)
     if x.dtype != np.float16:
         raise ValueError("activations are fp16")
@@ -152,6 +163,8 @@ def _as_rows(x: np.ndarray, k: int) -> np.ndarray:
         x = x[None, :]
     if x.ndim != 2 or x.shape[1] != k:
         raise ValueError(f"activations must be [m, {k}]")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("activations must be finite")
     return x.astype(np.float64)
 
 

@@ -15,6 +15,21 @@ bool bad_ffn(int64_t d_model, int64_t d_ff) {
   return d_model < 8 || d_model > PBG_FFN_MAX_MODEL || d_model % 8 != 0 || bad_nk(d_ff, d_model);
 }
 
+// True when earlier work on this thread left a HIP error pending. Such an
+// error is the caller's: it is left in place (not cleared) and the call
+// enqueues nothing. hipErrorNotReady from a completion query is a status,
+// not a failure, and is cleared so that the launch check below sees only
+// this call's errors.
+bool pending_error() {
+  const hipError_t e = hipPeekAtLastError();
+  if (e == hipSuccess) return false;
+  if (e == hipErrorNotReady) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return true;
+}
+
 int finish(hipError_t launch_status) {
   if (launch_status != hipSuccess) return PBG_ERR_HIP;
   return hipGetLastError() == hipSuccess ? PBG_OK : PBG_ERR_HIP;
@@ -45,7 +60,7 @@ int pack_ternary(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, in
   if (!codes || !packed || !row_sum || !stats) return PBG_ERR_NULL;
   if (bad_nk(n, k)) return PBG_ERR_SHAPE;
   if (misaligned(packed, 16) || misaligned(row_sum, 4) || misaligned(stats, 8)) return PBG_ERR_ALIGN;
-  (void)hipGetLastError();  // clear a stale error so the status below is this call's
+  if (pending_error()) return PBG_ERR_HIP;
   int rc = finish(pbg::launch_pack(codes, n, k, packed, row_sum, stats, stream));
   if (rc != PBG_OK || !stats_host) return rc;
   if (hipMemcpyAsync(stats_host, stats, 4 * sizeof(int64_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
@@ -59,7 +74,7 @@ int ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t 
   if (!packed || !scale || !x || !y) return PBG_ERR_NULL;
   if (bad_nk(n, k)) return PBG_ERR_SHAPE;
   if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_ternary_gemv(packed, scale, n, k, x, y, stream));
 }
 
@@ -68,7 +83,7 @@ int ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, in
   if (!packed || !scale || !x || !y) return PBG_ERR_NULL;
   if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
   if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_ternary_gemm_small(packed, scale, n, k, x, static_cast<int>(m), y, stream));
 }
 
@@ -77,7 +92,7 @@ int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, co
   if (!w || !scale || !x || !y) return PBG_ERR_NULL;
   if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
   if (misaligned(w, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_int8_head(w, scale, n, k, x, static_cast<int>(m), y, stream));
 }
 
@@ -88,7 +103,7 @@ int int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, 
   if (misaligned(w, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(keys, 8) || misaligned(token, 4) ||
       misaligned(logit, 4))
     return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_int8_head_argmax(w, scale, n, k, x, static_cast<int>(m),
                                              reinterpret_cast<unsigned long long*>(keys), token, logit, stream));
 }
@@ -98,7 +113,7 @@ int int8_embedding_gather(const int8_t* table, const float* scale, int64_t n, in
   if (!table || !scale || !tokens || !out) return PBG_ERR_NULL;
   if (bad_nk(n, k) || m < 1 || m > PBG_MAX_N || pbg::embedding_blocks(m, k) > (1LL << 23)) return PBG_ERR_SHAPE;
   if (misaligned(scale, 4) || misaligned(tokens, 4) || misaligned(out, 4)) return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_embedding_gather(table, scale, n, k, tokens, m, out, stream));
 }
 
@@ -106,7 +121,7 @@ int pbg_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t 
   if (!src || !sink) return PBG_ERR_NULL;
   if (bytes < 16 || bytes > PBG_STREAM_READ_MAX_BYTES || bytes % 16 != 0) return PBG_ERR_SHAPE;
   if (misaligned(src, 16) || misaligned(sink, 4)) return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_stream_read(src, bytes, sink, stream));
 }
 
@@ -118,7 +133,7 @@ int ternary_swiglu_gate_up(const uint32_t* gate_packed, const float* gate_scale,
   if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(gate_scale, 4) ||
       misaligned(up_scale, 4) || misaligned(x, 16) || misaligned(h, 16))
     return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_swiglu_gate_up(gate_packed, gate_scale, up_packed, up_scale, d_model, d_ff, x, h, stream));
 }
 
@@ -132,7 +147,7 @@ int ternary_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, con
       misaligned(gate_scale, 4) || misaligned(up_scale, 4) || misaligned(down_scale, 4) || misaligned(x, 16) ||
       misaligned(h, 16) || misaligned(y, 4))
     return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_ffn_swiglu(gate_packed, gate_scale, up_packed, up_scale, down_packed, down_scale, d_model,
                                        d_ff, x, h, y, stream));
 }
@@ -145,7 +160,7 @@ int ternary_swiglu_gate_up_small(const uint32_t* gate_packed, const float* gate_
   if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(gate_scale, 4) ||
       misaligned(up_scale, 4) || misaligned(x, 16) || misaligned(h, 16))
     return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_swiglu_gate_up_small(gate_packed, gate_scale, up_packed, up_scale, d_model, d_ff, x,
                                                  static_cast<int>(m), h, stream));
 }
@@ -161,7 +176,7 @@ int ternary_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scal
       misaligned(gate_scale, 4) || misaligned(up_scale, 4) || misaligned(down_scale, 4) || misaligned(x, 16) ||
       misaligned(h, 16) || misaligned(y, 4))
     return PBG_ERR_ALIGN;
-  (void)hipGetLastError();
+  if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_ffn_swiglu_small(gate_packed, gate_scale, up_packed, up_scale, down_packed, down_scale,
                                              d_model, d_ff, x, static_cast<int>(m), h, y, stream));
 }

@@ -165,10 +165,12 @@ __device__ __forceinline__ int reduce4_slot(int lane) {
 
 // Greedy-argmax key of a logit: the order-preserving image of the fp32 bits
 // in the high half and (2^32 - 1 - row) in the low half, so that the largest
-// key is the largest logit and, among equal logits, the lowest row. Logits
-// are finite.
+// key is the largest logit and, among equal logits, the lowest row. -0 is
+// keyed as +0 (the two compare equal, so the lower row must win between
+// them). Logits are finite.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int64_t row) {
-  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  uint32_t b = __builtin_bit_cast(uint32_t, v);
+  b = b == 0x80000000u ? 0u : b;
   const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   return (static_cast<unsigned long long>(ord) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(row));
 }

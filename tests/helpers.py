@@ -22,9 +22,15 @@ def ternary_bound(scale: np.ndarray, x: np.ndarray) -> np.ndarray:
     return TOL * np.abs(xs).sum(axis=1)[:, None] * np.abs(scale.astype(np.float64))[None, :]
 
 
-def head_bound(w: np.ndarray, scale: np.ndarray, x: np.ndarray) -> np.ndarray:
-    xs = np.atleast_2d(np.asarray(x, dtype=np.float64))
-    return TOL * (np.abs(xs) @ np.abs(w.astype(np.float64)).T) * np.abs(scale.astype(np.float64))[None, :]
+def head_bound(w: np.ndarray, scale: np.ndarray, x: np.ndarray, row_block: int = 16384) -> np.ndarray:
+    """Per-element bound [m, n] for int8 head outputs (rows in blocks to bound memory)."""
+    xs = np.abs(np.atleast_2d(np.asarray(x, dtype=np.float64)))
+    out = np.empty((xs.shape[0], w.shape[0]), dtype=np.float64)
+    for r0 in range(0, w.shape[0], row_block):
+        r1 = min(w.shape[0], r0 + row_block)
+        out[:, r0:r1] = TOL * (xs @ np.abs(w[r0:r1].astype(np.float64)).T) * np.abs(
+            scale[r0:r1].astype(np.float64))[None, :]
+    return out
 
 
 def assert_within(y, y_ref, bound, what=""):

@@ -45,6 +45,19 @@ def test_gate_up_launch_bytes():
     assert bench.gate_up_bytes(synth.FFN, synth.HIDDEN) == 25_296_896
 
 
+def test_ffn_block_bytes():
+    # the fused block as it runs: the gate|up launch, then down on the fp16 h
+    # (12,582,912 packed + 16,384 scales + 24,576 h in + 16,384 y out)
+    assert bench.ffn_block_bytes(synth.HIDDEN, synth.FFN) == 25_296_896 + 12_640_256 == 37_937_152
+    # three separate GEMVs would move 81,920 B more: x read twice more, g and u written as fp32
+    three = sum(bench.ternary_bytes(*synth.SHAPES[p]) for p in ("gate", "up", "down"))
+    assert three - bench.ffn_block_bytes(synth.HIDDEN, synth.FFN) == 81_920
+    # m rows: x and h scale with m, the weights do not
+    assert bench.ffn_block_bytes(synth.HIDDEN, synth.FFN, 8) == (3 * 12_582_912 + 2 * 4 * 12_288 + 4 * 4096
+                                                                 + 8 * (2 * 4096 + 2 * 12_288 + 2 * 12_288
+                                                                        + 4 * 4096))
+
+
 def test_more_than_one_gpu_is_refused():
     proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                           text=True, timeout=300, cwd=ROOT)

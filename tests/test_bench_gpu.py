@@ -28,17 +28,30 @@ def test_bench_json_line():
     assert d["vs_baseline"] is None
     assert d["config"]["workload"] == "ffn_gate_up_down_m1"
     assert d["value"] > 0 and d["ms_per_step"] > 0
-    # value is the step's algorithmic bytes over its time
-    step_bytes = 12_689_408 * 2 + 12_640_256
+    # value is the fused step's own algorithmic bytes over its time: the gate|up
+    # launch (x in, fp16 h out) and the down GEMV on h
+    step_bytes = 25_296_896 + 12_640_256
+    assert d["config"]["bytes_per_step"] == step_bytes
     assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]
+    # the same linears as three plain GEMVs, beside it
+    plain = d["config"]["plain_three_gemv"]
+    assert plain["bytes_per_step"] == 12_689_408 * 2 + 12_640_256
+    assert abs(plain["GBs"] - plain["bytes_per_step"] / (plain["us_per_step"] * 1e-6) / 1e9) <= 0.01 * plain["GBs"]
+    # the untimed work is stated
+    assert d["settle_steps"] > 0 and str(d["settle_steps"]) in d["config"]["untimed"]
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert 0 < r["achieved"] < r["peak"]
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert r["traffic"] is None or r["traffic"] > 25_296_896
+    assert r["traffic_note"].startswith("stored") == (r["traffic"] is not None)
     # the loads alone of the same packed bytes, one launch each
     assert 0 < r["read_ceiling_us"] and 0 < r["frac_of_read_ceiling"] < 1.5
     assert d["extra"]["stream_read_us"]["gate_12.6MB"] > 0
     c = d["cpu_baseline"]
-    assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0 and c["cores"] >= 1
+    assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0
+    assert c["cores"] == len(os.sched_getaffinity(0))  # the CPUs this process may use
+    assert 1 <= c["blas_threads"] <= c["cores"]
+    assert c["unpack_s"] > 0 and c["matvec_s"] > 0
+    assert abs(c["unpack_s"] + c["matvec_s"] - c["pass_s"]) <= 1e-4
     assert isinstance(c["sample"], str) and c["sample"]

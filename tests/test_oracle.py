@@ -200,6 +200,34 @@ def test_small_m_rows_equal_single_rows():
         assert np.array_equal(ym[m], oracle.ternary_gemv(packed, s, k, xs[m]))
 
 
+def test_oracle_rejects_non_finite_activations():
+    """Both sides require finite activations: the oracle raises on Inf or NaN
+    (whether or not the column's codes are zero), and still accepts and sums
+    exactly the largest finite fp16 values."""
+    k, n = 64, 3
+    codes = np.zeros((n, k), dtype=np.int8)
+    codes[1, 5] = 1
+    packed = oracle.pack(codes)[0]
+    s = np.ones(n, dtype=np.float32)
+    w = np.ones((n, k), dtype=np.int8)
+    for bad in (np.inf, -np.inf, np.nan):
+        x = np.zeros((2, k), dtype=np.float16)
+        x[1, 0] = bad  # every code of column 0 is zero
+        with pytest.raises(ValueError, match="finite"):
+            oracle.ternary_gemm_small(packed, s, k, x)
+        with pytest.raises(ValueError, match="finite"):
+            oracle.ternary_gemv(packed, s, k, x[1])
+        with pytest.raises(ValueError, match="finite"):
+            oracle.int8_head_gemv(w, s, x)
+        with pytest.raises(ValueError, match="finite"):
+            oracle.int8_head_argmax(w, s, x)
+    big = np.float16(65504.0)
+    x = np.full(k, big, dtype=np.float16)
+    x[7] = -big
+    y = oracle.ternary_gemv(oracle.pack(np.ones((n, k), dtype=np.int8))[0], s, k, x)
+    assert np.all(y == (k - 2) * 65504.0)
+
+
 def test_integer_probe_exact():
     """Integer activations and power-of-two scales: y is an exact integer
     multiple of the scale, equal to the integer matmul."""

@@ -11,6 +11,8 @@ counts). Floating-point outputs are compared
 """
 from __future__ import annotations
 
+import ctypes
+import os
 import sys
 
 import numpy as np
@@ -349,6 +351,46 @@ def test_device_error_paths(pbg):
     assert torch.all(y == 0)
 
 
+def _loaded_hip_runtimes():
+    """ctypes handles of every HIP runtime mapped into this process."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1] if len(line.split()) >= 6 else ""
+            if "libamdhip64" in os.path.basename(path):
+                paths.add(path)
+    return [ctypes.CDLL(p) for p in sorted(paths)]
+
+
+def test_pending_hip_error_is_left_to_the_caller(pbg):
+    """A HIP error left pending by earlier work (here a host-side query of a
+    device that does not exist) is the caller's: an entry point then
+    enqueues nothing, returns PBG_ERR_HIP and leaves the error pending."""
+    lib = pbg.lib()
+    p = torch.zeros((8, 4), dtype=torch.int32, device="cuda:0")
+    s = torch.ones(8, dtype=torch.float32, device="cuda:0")
+    x = torch.ones(64, dtype=torch.float16, device="cuda:0")
+    y = torch.full((8,), 7.0, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    hips = _loaded_hip_runtimes()
+    assert hips, "no HIP runtime mapped"
+    v = ctypes.c_int(0)
+    for h in hips:
+        assert h.hipDeviceGetAttribute(ctypes.byref(v), 0, 9999) != 0
+    pending = [h.hipPeekAtLastError() for h in hips]
+    assert all(e != 0 for e in pending)
+    assert lib.ternary_gemv(p.data_ptr(), s.data_ptr(), 8, 64, x.data_ptr(), y.data_ptr(), stream) == -5
+    assert [h.hipPeekAtLastError() for h in hips] == pending  # still the caller's to see
+    for h in hips:
+        h.hipGetLastError()
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)  # nothing was enqueued
+    assert lib.ternary_gemv(p.data_ptr(), s.data_ptr(), 8, 64, x.data_ptr(), y.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
 # --------------------------------------------------------------------------
 # HIP graph capture and replay
 # --------------------------------------------------------------------------
@@ -419,6 +461,27 @@ def test_head_argmax_exact_probe(pbg, m, n, k):
     assert np.array_equal(logit.cpu().numpy().astype(np.float64), y_ref[np.arange(m), tok_ref])
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 8])
+@pytest.mark.parametrize("n,k", [(33, 4112), (40, 4096), (2000, 4096), (40000, 1024)])
+def test_head_argmax_signed_zero_tie(pbg, m, n, k):
+    """A zero maximum reached as -0 by a lower row (negative scale) and as +0
+    by a higher row: the two logits are equal, so the lower row is the token,
+    as in the oracle. Every other logit is -k."""
+    say(f"argmax signed zero m={m} n={n} k={k}")
+    w = np.full((n, k), -1, dtype=np.int8)
+    lo, hi = n // 3, n // 3 + 7
+    w[lo] = 0
+    w[hi] = 0
+    x = np.ones((m, k), dtype=np.float16)
+    s = np.ones(n, dtype=np.float32)
+    s[lo] = -1.0
+    tok_ref, y_ref = oracle.int8_head_argmax(w, s, x)
+    assert tok_ref.tolist() == [lo] * m
+    tok, logit = pbg.int8_head_argmax(dev(w), dev(s), dev(x))
+    assert tok.cpu().numpy().tolist() == [lo] * m
+    assert np.all(logit.cpu().numpy() == 0.0)
+
+
 @pytest.mark.parametrize("m", [1, 2, 4, 7, 8])
 def test_head_argmax_random(pbg, m):
     n, k = 5003, 4096
@@ -456,14 +519,21 @@ def test_head_argmax_full_size(pbg, m):
     for i in range(m):
         assert tok[i] == int(np.argmax(y[i]))
         assert logit.cpu().numpy()[i] == y[i, tok[i]]
-    # the chosen rows against the oracle
-    rows = torch.from_numpy(tok.astype(np.int64)).to("cuda:0")
-    w_rows = w[rows].cpu().numpy()
-    s_rows = s.cpu().numpy()[tok]
-    ref = oracle.int8_head_gemv(w_rows, s_rows, x)
-    b = head_bound(w_rows, s_rows, x)
+    # the token against the fp64 oracle over every row of the head: a valid
+    # argmax of the exact logits within their error bounds, and the oracle's
+    # own token whenever its top-2 gap exceeds twice the largest bound
+    w_host, s_host = w.cpu().numpy(), s.cpu().numpy()
+    tok_ref, y_ref = oracle.int8_head_argmax(w_host, s_host, x)
+    bound = head_bound(w_host, s_host, x)
+    lg = logit.cpu().numpy()
     for i in range(m):
-        assert abs(float(logit.cpu().numpy()[i]) - ref[i, i]) <= b[i, i]
+        t = int(tok[i])
+        assert y_ref[i, t] >= np.max(y_ref[i] - bound[i]) - bound[i, t], (i, t, int(tok_ref[i]))
+        assert abs(float(lg[i]) - y_ref[i, t]) <= bound[i, t]
+        top = np.sort(y_ref[i])
+        if top[-1] - top[-2] > 2 * bound[i].max():
+            assert t == int(tok_ref[i]), (i, t, int(tok_ref[i]))
+    say(f"  tokens {tok.tolist()}, oracle {tok_ref.tolist()}")
 
 
 def test_head_argmax_workspace_reuse_and_graph(pbg):
