@@ -171,6 +171,26 @@ int int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, 
                      uint64_t* keys, int32_t* token, float* logit, hipStream_t stream);
 
 /*
+ * int8_head_argmax_noalloc - int8_head_argmax for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation): the same computation and results, with
+ * the keys workspace replaced by a device array the library owns.
+ *
+ *   w, scale, n, k, x, m, token, logit  as int8_head_argmax
+ *   1 <= m <= PBG_MAX_M; a larger m returns PBG_ERR_SHAPE
+ * The array holds the keys of PBG_MAX_M rows (PBG_NOALLOC_SCRATCH_BYTES =
+ * 256 KiB) on every GPU the library runs on and is kept until the process
+ * ends. It starts zeroed and every call leaves it zero again. The call
+ * allocates and frees nothing. All calls on one GPU share the array: calls
+ * that overlap in time (other streams, other threads) race and their tokens
+ * are then unspecified; calls ordered on one stream are safe.
+ */
+#define PBG_NOALLOC_SCRATCH_BYTES (PBG_MAX_M * PBG_ARGMAX_KEYS_PER_ROW * 8)
+
+int int8_head_argmax_noalloc(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                             int64_t m, int32_t* token, float* logit, hipStream_t stream);
+
+/*
  * int8_embedding_gather - out[i][j] = scale[t] * table[t][j] with t =
  * tokens[i], formed exactly and rounded once to fp32.
  * Source: Neutrino-1 8B model page, "Where the bytes live" (untied int8 input

@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     PbgError,
     int8_embedding_gather,
     int8_head_argmax,
+    int8_head_argmax_noalloc,
     int8_head_gemv,
     lib,
     pack_ternary,
@@ -23,6 +24,7 @@ __all__ = [
     "PbgError",
     "int8_embedding_gather",
     "int8_head_argmax",
+    "int8_head_argmax_noalloc",
     "int8_head_gemv",
     "lib",
     "pack_ternary",

@@ -34,6 +34,7 @@ _SIGNATURES = {
     "ternary_gemm_small": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "int8_head_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "int8_head_argmax": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _vp, _vp]),
+    "int8_head_argmax_noalloc": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _vp]),
     "int8_embedding_gather": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "ternary_swiglu_gate_up": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "ternary_ffn_swiglu": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
@@ -228,6 +229,34 @@ def int8_head_argmax(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, keys
     rc = lib().int8_head_argmax(w.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, keys.data_ptr(),
                                 token.data_ptr(), logit.data_ptr(), _stream(w))
     _check("int8_head_argmax", rc)
+    return token, logit
+
+
+def int8_head_argmax_noalloc(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor,
+                             token: torch.Tensor | None = None, logit: torch.Tensor | None = None):
+    """int8_head_argmax with the library's own workspace: (token int32 [m], logit fp32 [m]).
+
+    The C call allocates nothing (pass token and logit to keep this wrapper from allocating
+    them). Calls that overlap in time on one GPU race.
+    """
+    _dev(w, "w", torch.int8)
+    _dev(scale, "scale", torch.float32)
+    _dev(x, "x", torch.float16)
+    if w.dim() != 2 or x.dim() != 2 or x.shape[1] != w.shape[1] or tuple(scale.shape) != (w.shape[0],):
+        raise ValueError("w [n, k], scale [n], x [m, k]")
+    n, k = w.shape
+    m = x.shape[0]
+    if token is None:
+        token = torch.empty((m,), dtype=torch.int32, device=w.device)
+    if logit is None:
+        logit = torch.empty((m,), dtype=torch.float32, device=w.device)
+    _dev(token, "token", torch.int32)
+    _dev(logit, "logit", torch.float32)
+    if token.numel() != m or logit.numel() != m:
+        raise ValueError("token and logit hold m entries")
+    rc = lib().int8_head_argmax_noalloc(w.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, token.data_ptr(),
+                                        logit.data_ptr(), _stream(w))
+    _check("int8_head_argmax_noalloc", rc)
     return token, logit
 
 

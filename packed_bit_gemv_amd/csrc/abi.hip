@@ -108,6 +108,16 @@ int int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, 
                                              reinterpret_cast<unsigned long long*>(keys), token, logit, stream));
 }
 
+int int8_head_argmax_noalloc(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                             int64_t m, int32_t* token, float* logit, hipStream_t stream) {
+  if (!w || !scale || !x || !token) return PBG_ERR_NULL;
+  if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(w, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(token, 4) || misaligned(logit, 4))
+    return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_int8_head_argmax_noalloc(w, scale, n, k, x, static_cast<int>(m), token, logit, stream));
+}
+
 int int8_embedding_gather(const int8_t* table, const float* scale, int64_t n, int64_t k, const int32_t* tokens,
                           int64_t m, float* out, hipStream_t stream) {
   if (!table || !scale || !tokens || !out) return PBG_ERR_NULL;

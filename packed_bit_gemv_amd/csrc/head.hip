@@ -632,4 +632,47 @@ hipError_t launch_int8_head_argmax(const int8_t* w, const float* scale, int64_t 
   return hipGetLastError();
 }
 
+// Bins of int8_head_argmax_noalloc: the keys workspace of PBG_MAX_M rows in
+// device memory the library owns (256 KiB on every GPU it runs on, held until
+// the process ends). Code-object storage starts zeroed, and every call's
+// finishing kernel sets the bins it read back to zero, so the array is zero
+// whenever no call is in flight. Calls that overlap in time on one GPU share
+// it and race.
+static __device__ __align__(256) unsigned long long scratch[PBG_MAX_M * PBG_ARGMAX_KEYS_PER_ROW];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device. In host code the array's name only stands in for the symbol, so
+// kernels are handed this address, never the name.
+hipError_t scratch_address(unsigned long long** out) {
+  static std::atomic<unsigned long long*> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  unsigned long long* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<unsigned long long*>(addr);
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_int8_head_argmax_noalloc(const int8_t* w, const float* scale, int64_t n, int64_t k,
+                                           const uint16_t* x, int m, int32_t* token, float* logit,
+                                           hipStream_t stream) {
+  if (m < 1 || m > PBG_MAX_M) return hipErrorInvalidValue;
+  unsigned long long* keys = nullptr;
+  const hipError_t e = scratch_address(&keys);
+  if (e != hipSuccess) return e;
+  return launch_int8_head_argmax(w, scale, n, k, x, m, keys, token, logit, stream);
+}
+
 }  // namespace pbg

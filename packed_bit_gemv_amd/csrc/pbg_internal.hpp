@@ -21,6 +21,11 @@ hipError_t launch_int8_head(const int8_t* w, const float* scale, int64_t n, int6
 hipError_t launch_int8_head_argmax(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
                                    int m, unsigned long long* keys, int32_t* token, float* logit, hipStream_t stream);
 
+// int8_head_argmax with its keys in the library's own device array (allocates nothing).
+hipError_t launch_int8_head_argmax_noalloc(const int8_t* w, const float* scale, int64_t n, int64_t k,
+                                           const uint16_t* x, int m, int32_t* token, float* logit,
+                                           hipStream_t stream);
+
 hipError_t launch_embedding_gather(const int8_t* table, const float* scale, int64_t n, int64_t k,
                                    const int32_t* tokens, int64_t m, float* out, hipStream_t stream);
 

@@ -54,6 +54,10 @@ int main(void) {
   expect("argmax keys misaligned", int8_head_argmax(w, scale, 8, 64, x, 1, (uint64_t*)(base + 0x5004), token,
                                                     y, 0), PBG_ERR_ALIGN);
   expect("argmax null token", int8_head_argmax(w, scale, 8, 64, x, 1, keys, NULL, y, 0), PBG_ERR_NULL);
+  expect("argmax noalloc m = 9", int8_head_argmax_noalloc(w, scale, 8, 64, x, PBG_MAX_M + 1, token, y, 0),
+         PBG_ERR_SHAPE);
+  expect("argmax noalloc null w", int8_head_argmax_noalloc(NULL, scale, 8, 64, x, 1, token, y, 0), PBG_ERR_NULL);
+  expect("argmax noalloc scratch size", PBG_NOALLOC_SCRATCH_BYTES, 262144);
   expect("embedding m = 0", int8_embedding_gather(w, scale, 8, 64, tokens, 0, y, 0), PBG_ERR_SHAPE);
   expect("pack null codes", pack_ternary(NULL, 8, 64, (uint32_t*)base, (int32_t*)(base + 0x1000), NULL, NULL, 0),
          PBG_ERR_NULL);
