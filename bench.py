@@ -254,10 +254,16 @@ def main():
     ys = {p: torch.empty((8, synth.SHAPES[p][0]), dtype=torch.float32, device=device) for p in synth.PROJECTIONS}
     L = len(model.layers)
 
+    # split-K workspace for the down projection at m >= 2 (the entry point
+    # splits only where it measured faster, else runs ternary_gemm_small)
+    ws_down = pbg.splitk_workspace(*synth.SHAPES["down"], device)
+
     def linear(layer, p, m=1):
         packed, s, n, k = model.layers[layer][p]
         if m == 1:
             pbg.ternary_gemv(packed, s, k, xs[k][0], ys[p][0])
+        elif p == "down":
+            pbg.ternary_gemm_splitk(packed, s, k, xs[k][:m], ws_down, ys[p][:m])
         else:
             pbg.ternary_gemm_small(packed, s, k, xs[k][:m], ys[p][:m])
 
@@ -419,6 +425,15 @@ def main():
         extra["decode_step_m1_GBs"] = round(dec_bytes / (ms * 1e-3) / 1e9, 1)
         del g
 
+        # the down projection alone at m = 8: the plain small-M GEMM and the K-split one
+        for label, fn in (("down_m8_plain_us", lambda l: pbg.ternary_gemm_small(
+                              model.layers[l]["down"][0], model.layers[l]["down"][1], synth.FFN, xs[synth.FFN][:8],
+                              ys["down"][:8])),
+                          ("down_m8_splitk_us", lambda l: linear(l, "down", 8))):
+            g = capture(torch, lambda fn=fn: [fn(l) for l in range(L)])
+            extra[label] = round(time_graphs(torch, [g], 5, 1) * 1e3 / L, 3)
+            del g
+
         for m in (2, 4, 7, 8):
             graphs = [capture(torch, lambda l=l, m=m: layer_step(l, m)) for l in range(L)]
             ms = time_graphs(torch, graphs, K, W)
@@ -515,8 +530,10 @@ def main():
             pbg.ternary_gemm_small(qp, qs, synth.HIDDEN, xs[synth.HIDDEN][:m], yqkv_m[:m])
             linear(l, "o", m)
             lay = model.layers[l]
-            pbg.ternary_ffn_swiglu(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], lay["down"][0],
-                                   lay["down"][1], xs[synth.HIDDEN][:m], h_m[:m], y_m[:m])
+            # the block: gate|up + SwiGLU for m rows, then down on h (split over K where that is faster)
+            pbg.ternary_swiglu_gate_up(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], synth.HIDDEN,
+                                       xs[synth.HIDDEN][:m], h_m[:m])
+            pbg.ternary_gemm_splitk(lay["down"][0], lay["down"][1], synth.FFN, h_m[:m], ws_down, y_m[:m])
 
         for m in (2, 4, 7, 8):
             graphs = [capture(torch, lambda l=l, m=m: fused_layer_m(l, m)) for l in range(L)]

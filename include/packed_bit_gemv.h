@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define PBG_ABI_VERSION 1
+#define PBG_ABI_VERSION 2
 
 /* Return codes. */
 #define PBG_OK 0
@@ -70,6 +70,7 @@ extern "C" {
 #define PBG_ERR_ALIGN (-3)   /* a pointer lacks its required alignment */
 #define PBG_ERR_CODE (-4)    /* pack input held a value outside {-1, 0, +1} */
 #define PBG_ERR_HIP (-5)     /* a HIP launch or copy failed */
+#define PBG_ERR_WORKSPACE (-6) /* a workspace is smaller than the call needs */
 
 /* Limits: 1 <= n <= PBG_MAX_N, 1 <= k <= PBG_MAX_K, 1 <= m <= PBG_MAX_M. */
 #define PBG_MAX_N 16777216LL
@@ -129,6 +130,41 @@ int ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t 
  */
 int ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
                        int64_t m, float* y, hipStream_t stream);
+
+/*
+ * ternary_gemm_splitk - ternary_gemm_small (1 <= m <= 8 activation rows) with
+ * the K columns also split across workgroups, for matrices whose few rows or
+ * long rows would leave the plain kernels short of workgroups or re-reading
+ * all of x per row block (a 1,024 x 12,288 shard of the down projection, the
+ * full 4,096 x 12,288 one at m = 8). Each slice of a row block adds its
+ * partial sums into one 64-bit integer per output in the workspace (exact
+ * fixed point with 23 fractional bits; the low 4 bits count arrivals); the
+ * slice that completes an output writes it and sets the integer back to
+ * zero. No workgroup waits for another, and the result is the exact sum of
+ * the slices' fp32 partials rounded once, whatever order they arrive in, so
+ * it is bitwise repeatable (its summation order differs from
+ * ternary_gemm_small's).
+ * Source: Neutrino-1 8B model page, introduction (decode speed is set by the
+ * bytes a step moves), geometry table (feed-forward width 12,288) and
+ * "speculative" section (several drafted positions in one pass).
+ *
+ *   packed, scale, n, k, x, m, y  as ternary_gemm_small; activations must
+ *              be finite with |x| <= 65,504 (any finite fp16)
+ *   workspace  device, 256-byte aligned, owned by the caller, at least
+ *              pbg_splitk_workspace_bytes(n, k) bytes (enough for every m),
+ *              all zero before its first use (e.g. one zero fill at
+ *              allocation); every call leaves it all zero again. Calls that
+ *              overlap in time need separate workspaces.
+ *   workspace_bytes  its size; PBG_ERR_WORKSPACE if too small
+ * The split runs where it measured faster on MI355X: m >= 2 with
+ * 4,096 < k <= 16,384, k % 8 == 0, x 16-byte aligned, and n <= 2,048, or
+ * n <= 4,096 with k <= 12,288 and m >= 5. Other calls run ternary_gemm_small's
+ * kernels and leave the workspace untouched.
+ */
+int64_t pbg_splitk_workspace_bytes(int64_t n, int64_t k);
+
+int ternary_gemm_splitk(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                        int64_t m, float* y, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * int8_head_gemv - Y[i][v] = scale[v] * sum_j w[v][j] * X[i][j] for the int8

@@ -12,10 +12,12 @@ from .binding import (  # noqa: F401
     int8_head_gemv,
     lib,
     pack_ternary,
+    splitk_workspace,
     stream_read,
     ternary_ffn_swiglu,
     ternary_swiglu_gate_up,
     ternary_gemm_small,
+    ternary_gemm_splitk,
     ternary_gemv,
     words_per_row,
 )
@@ -28,10 +30,12 @@ __all__ = [
     "int8_head_gemv",
     "lib",
     "pack_ternary",
+    "splitk_workspace",
     "stream_read",
     "ternary_ffn_swiglu",
     "ternary_swiglu_gate_up",
     "ternary_gemm_small",
+    "ternary_gemm_splitk",
     "ternary_gemv",
     "words_per_row",
 ]

@@ -32,6 +32,8 @@ _SIGNATURES = {
     "pack_ternary": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "ternary_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "ternary_gemm_small": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "pbg_splitk_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
+    "ternary_gemm_splitk": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64, _vp]),
     "int8_head_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "int8_head_argmax": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _vp, _vp]),
     "int8_head_argmax_noalloc": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _vp]),
@@ -173,6 +175,37 @@ def ternary_gemm_small(packed: torch.Tensor, scale: torch.Tensor, k: int, x: tor
     rc = lib().ternary_gemm_small(packed.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, y.data_ptr(),
                                   _stream(packed))
     _check("ternary_gemm_small", rc)
+    return y
+
+
+def splitk_workspace(n: int, k: int, device) -> torch.Tensor:
+    """A zeroed workspace for ternary_gemm_splitk on [n, k] matrices (any m)."""
+    nbytes = int(lib().pbg_splitk_workspace_bytes(int(n), int(k)))
+    return torch.zeros(((nbytes + 7) // 8,), dtype=torch.int64, device=device)
+
+
+def ternary_gemm_splitk(packed: torch.Tensor, scale: torch.Tensor, k: int, x: torch.Tensor, workspace: torch.Tensor,
+                        y: torch.Tensor | None = None) -> torch.Tensor:
+    """ternary_gemv (x [k] -> y [n]) or ternary_gemm_small (x [m, k] -> y [m, n]) with K split
+    across workgroups; workspace from splitk_workspace(n, k), reused across calls."""
+    n = _ternary_args(packed, scale, k, x)
+    if x.dim() == 1 and x.shape[0] == k:
+        m, y_shape = 1, (n,)
+    elif x.dim() == 2 and x.shape[1] == k:
+        m, y_shape = x.shape[0], (x.shape[0], n)
+    else:
+        raise ValueError(f"x must be [{k}] or [m, {k}]")
+    if y is None:
+        y = torch.empty(y_shape, dtype=torch.float32, device=packed.device)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != y_shape:
+        raise ValueError(f"y must be {list(y_shape)}")
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA (HIP) tensor")
+    rc = lib().ternary_gemm_splitk(packed.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, y.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(packed))
+    _check("ternary_gemm_splitk", rc)
     return y
 
 

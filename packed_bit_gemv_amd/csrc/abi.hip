@@ -49,6 +49,7 @@ const char* pbg_strerror(int code) {
     case PBG_ERR_ALIGN: return "a pointer lacks its required alignment";
     case PBG_ERR_CODE: return "pack input held a value outside {-1, 0, +1}";
     case PBG_ERR_HIP: return "a HIP launch or copy failed";
+    case PBG_ERR_WORKSPACE: return "workspace smaller than the call needs";
     default: return "unknown error code";
   }
 }
@@ -85,6 +86,24 @@ int ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, in
   if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
   if (pending_error()) return PBG_ERR_HIP;
   return finish(pbg::launch_ternary_gemm_small(packed, scale, n, k, x, static_cast<int>(m), y, stream));
+}
+
+int64_t pbg_splitk_workspace_bytes(int64_t n, int64_t k) {
+  if (bad_nk(n, k)) return 0;
+  return pbg::splitk_workspace_bytes(n, k);
+}
+
+int ternary_gemm_splitk(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                        int64_t m, float* y, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (!packed || !scale || !x || !y || !workspace) return PBG_ERR_NULL;
+  if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4) ||
+      misaligned(workspace, 256))
+    return PBG_ERR_ALIGN;
+  if (workspace_bytes < pbg::splitk_workspace_bytes(n, k)) return PBG_ERR_WORKSPACE;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_ternary_gemm_splitk(packed, scale, n, k, x, static_cast<int>(m), y, workspace,
+                                                workspace_bytes, stream));
 }
 
 int int8_head_gemv(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, int64_t m,

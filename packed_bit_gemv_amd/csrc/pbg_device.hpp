@@ -184,6 +184,38 @@ __device__ __forceinline__ int32_t argmax_key_row(unsigned long long key) {
   return static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
+// K split across workgroups. The S slices of a row block meet in one 64-bit
+// integer per output (in a caller workspace that is zero between calls):
+// each slice adds its fp32 partial, converted exactly to fixed point with 23
+// fractional bits, shifted left by 4, plus 1 in the low 4 bits, which count
+// arrivals. The add that brings the count to S returns the sum of all the
+// others, so that workgroup adds its own, writes the output and sets the
+// accumulator back to zero; no workgroup waits for another. Integer addition
+// is exact and associative, so the result does not depend on the order of
+// arrival: it is the exact sum of the S fp32 partials, rounded once to fp32.
+// Exactness of the conversion: products 2 * c * x of fp16 activations are
+// multiples of 2^-23, so every fp32 partial of them is too, and |partial| <
+// 2^31 for K <= 16,384 (|x| <= 65,504), so partial * 2^23 is an integer below
+// 2^54 and S <= 15 of them, times 16, stay below 2^63.
+struct SplitK {
+  unsigned long long* acc;  // [row blocks][outputs per workgroup]
+  int S;                    // slices, 1 <= S <= 15
+};
+
+constexpr float kFix = 8388608.0f;  // 2^23
+
+// Adds `partial` (slice contribution to one output) to its accumulator; true
+// for the last of the S slices, which then gets the full sum in `total`.
+__device__ __forceinline__ bool splitk_add(unsigned long long* acc, float partial, int S, float& total) {
+  const long long fx = static_cast<long long>(partial * kFix);
+  const unsigned long long add = (static_cast<unsigned long long>(fx) << 4) + 1ull;
+  const unsigned long long before = __hip_atomic_fetch_add(acc, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (static_cast<int>(before & 15ull) != S - 1) return false;
+  __hip_atomic_store(acc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  total = static_cast<float>(static_cast<long long>(before + add) >> 4) * (1.0f / kFix);
+  return true;
+}
+
 // Loads x[base .. base+2*NPAIR-1] as NPAIR fp16 pairs; columns >= k read 0.
 template <int NPAIR>
 __device__ __forceinline__ void load_x_pairs(const uint16_t* __restrict__ x, int64_t k, int64_t base,

@@ -15,6 +15,16 @@ hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64
 hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
                                      const uint16_t* x, int m, float* y, hipStream_t stream);
 
+// ternary_gemm_small with K split across workgroups (1 <= m <= 8); the
+// slices meet in `ws` (splitk_workspace_bytes(n, k) bytes, zero before the
+// first call, left ready by every call). Shapes that are not split run the
+// plain dispatch.
+constexpr int64_t kSplitMaxK = 16384;
+int64_t splitk_workspace_bytes(int64_t n, int64_t k);
+hipError_t launch_ternary_gemm_splitk(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                      const uint16_t* x, int m, float* y, void* ws, int64_t ws_bytes,
+                                      hipStream_t stream);
+
 hipError_t launch_int8_head(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
                             int m, float* y, hipStream_t stream);
 

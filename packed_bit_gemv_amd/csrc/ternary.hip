@@ -33,7 +33,10 @@ constexpr int kGemvWaves = 4;
 //     rows, so every activation is read from LDS once per wave.
 //  4. One transposed reduction over the wave finishes the R rows.
 // Splitting K across the waves of a workgroup instead (and adding the slices
-// in LDS) measured 9-25 % slower for CPL = 2..4 on MI355X.
+// in LDS) measured 9-25 % slower for CPL = 2..4 on MI355X, and across
+// workgroups (ternary_gemm_splitk's scheme) no faster at one activation row:
+// the combine's atomic round trip ends the launch later than the shorter
+// activation staging saves.
 template <int CPL, int G, int R>
 __global__ __launch_bounds__(G* kWave) void ternary_gemv_kernel(const uint4* __restrict__ packed,
                                                                 const float* __restrict__ scale, int64_t n,
@@ -298,12 +301,15 @@ __global__ __launch_bounds__(kGemvWaves* kWave) void ternary_gemm_small_kernel(c
 // j mod MP, conflict-free. Columns j >= M are discarded in the epilogue.
 // A workgroup holds SK waves that split the units of T tiles; their partial
 // tiles meet in LDS and are added in wave order.
-template <int SK, int T, int UPW, int MP>
+// SPLIT: K is also split across workgroups; blockIdx.y is the slice of
+// SK * UPW units (starting at unit blockIdx.y * SK * UPW), and the slices of
+// a row block meet through `sp` (SplitK).
+template <int SK, int T, int UPW, int MP, bool SPLIT>
 __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint4* __restrict__ packed,
                                                                        const float* __restrict__ scale,
                                                                        int64_t n, int64_t k, int64_t chunks,
                                                                        const uint16_t* __restrict__ x, int m,
-                                                                       float* __restrict__ y) {
+                                                                       float* __restrict__ y, SplitK sp) {
   typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
   typedef float float4_t __attribute__((ext_vector_type(4)));
   constexpr int kRows = 16 * T;
@@ -313,6 +319,7 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
   const int li = lane & 15, lg = lane >> 4;
   const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kRows;
   const int64_t groups = k / 8;  // 8-column activation groups
+  const int64_t u0 = SPLIT ? static_cast<int64_t>(blockIdx.y) * SK * UPW : 0;  // first unit of the slice
   const uint4* xg = reinterpret_cast<const uint4*>(x);
 
   // Outputs (row, column) o = threadIdx.x + e * SK * 64 of the tile block,
@@ -334,7 +341,7 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
   __shared__ uint4 xs[SK][2][MP * kSlots];
   const int xrow = li >> 3, xg8 = li & 7;
   auto load_x = [&](int q, uint4 (&xr)[kXLoads]) {
-    const int64_t u = s + static_cast<int64_t>(SK) * q;
+    const int64_t u = u0 + s + static_cast<int64_t>(SK) * q;
 #pragma unroll
     for (int a = 0; a < kXLoads; ++a) {
       const int row = 2 * a + xrow;
@@ -343,14 +350,14 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
     }
   };
   auto stage_x = [&](int q, const uint4 (&xr)[kXLoads]) {
-    const int64_t gi = 32 * (s + static_cast<int64_t>(SK) * q) + 8 * lg + xg8;
+    const int64_t gi = 32 * (u0 + s + static_cast<int64_t>(SK) * q) + 8 * lg + xg8;
 #pragma unroll
     for (int a = 0; a < kXLoads; ++a)
       xs[s][q & 1][(2 * a + xrow) * kSlots + 8 * lg + xg8] = masked(xr[a], gi < groups);
   };
   // one 16-byte chunk of A per tile
   auto load_w = [&](int q, uint4 (&wv)[T]) {
-    const int64_t c = 4 * (s + static_cast<int64_t>(SK) * q) + lg;
+    const int64_t c = 4 * (u0 + s + static_cast<int64_t>(SK) * q) + lg;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t r = row_base + 16 * t + li;
@@ -403,16 +410,29 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
       for (int r = 0; r < 4; ++r) part[s][16 * t + 4 * lg + r][li] = d[t][r];
   }
   __syncthreads();
+  float sum[kOut];
 #pragma unroll
   for (int e = 0; e < kOut; ++e) {
     const int o = threadIdx.x + e * SK * kWave;
     const int orow = o >> 3, ocol = o & 7;
     const int64_t r = row_base + orow;
+    sum[e] = 0.0f;
     if (o < kRows * 8 && ocol < m && r < n) {
-      float sum = part[0][orow][ocol];
+      sum[e] = part[0][orow][ocol];
 #pragma unroll
-      for (int w = 1; w < SK; ++w) sum += part[w][orow][ocol];
-      y[static_cast<int64_t>(ocol) * n + r] = sum * (sc[e] * kCodeUnitInv);
+      for (int w = 1; w < SK; ++w) sum[e] += part[w][orow][ocol];
+      if constexpr (!SPLIT) y[static_cast<int64_t>(ocol) * n + r] = sum[e] * (sc[e] * kCodeUnitInv);
+    }
+  }
+  if constexpr (SPLIT) {
+    unsigned long long* acc = sp.acc + static_cast<int64_t>(blockIdx.x) * (kRows * 8);
+#pragma unroll
+    for (int e = 0; e < kOut; ++e) {
+      const int o = threadIdx.x + e * SK * kWave;
+      const int64_t r = row_base + (o >> 3);
+      float total;
+      if (o < kRows * 8 && (o & 7) < m && r < n && splitk_add(acc + o, sum[e], sp.S, total))
+        y[static_cast<int64_t>(o & 7) * n + r] = total * (sc[e] * kCodeUnitInv);
     }
   }
 }
@@ -430,8 +450,9 @@ template <int SK, int T, int UPW, int MP>
 void launch_mfma_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
                     float* y, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
-  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP>), grid, dim3(SK * kWave), 0, stream,
-                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y);
+  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP, false>), grid, dim3(SK * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y,
+                     SplitK{nullptr, 1});
 }
 
 // MP = m rounded up to 2, 4 or 8: the activation rows one x slice holds.
@@ -452,7 +473,59 @@ void launch_small(const uint32_t* packed, const float* scale, int64_t n, int64_t
                      words_per_row(k), x, y);
 }
 
+// Split-K launches: grid (row blocks, slices). A row block's accumulators
+// follow those of the row blocks before it, 8 bytes per output.
+template <int SK, int T, int UPW, int MP>
+hipError_t launch_mfma_split_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                                int m, float* y, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  const int64_t units = (words_per_row(k) / 4 + 3) / 4;
+  const int64_t nrb = (n + 16 * T - 1) / (16 * T);
+  const int slices = static_cast<int>((units + SK * UPW - 1) / (SK * UPW));
+  if (slices > 15 || 8 * nrb * (16 * T * 8) > ws_bytes) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP, true>), dim3(static_cast<unsigned>(nrb), slices),
+                     dim3(SK * kWave), 0, stream, reinterpret_cast<const uint4*>(packed), scale, n, k,
+                     words_per_row(k) / 4, x, m, y, SplitK{static_cast<unsigned long long*>(ws), slices});
+  return hipGetLastError();
+}
+
+template <int SK, int T, int UPW>
+hipError_t launch_mfma_split(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                             int m, float* y, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  if (m <= 2) return launch_mfma_split_mp<SK, T, UPW, 2>(packed, scale, n, k, x, m, y, ws, ws_bytes, stream);
+  if (m <= 4) return launch_mfma_split_mp<SK, T, UPW, 4>(packed, scale, n, k, x, m, y, ws, ws_bytes, stream);
+  return launch_mfma_split_mp<SK, T, UPW, 8>(packed, scale, n, k, x, m, y, ws, ws_bytes, stream);
+}
+
 }  // namespace
+
+int64_t splitk_workspace_bytes(int64_t n, int64_t /*k*/) {
+  // one 8-byte accumulator per output of a row block (at most 8 activation
+  // rows, row blocks of at most 64 rows)
+  return 8 * 8 * (n + 64);
+}
+
+hipError_t launch_ternary_gemm_splitk(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                      const uint16_t* x, int m, float* y, void* ws, int64_t ws_bytes,
+                                      hipStream_t stream) {
+  const bool fast = k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
+  // Split where graph-timed sweeps on MI355X measured it faster than the
+  // plain dispatch (pools of 36 matrices, m = 2..8, both orders; us plain /
+  // split): n <= 2,048 at every m (1,024 x 12,288: 5.01 / 4.10 at m = 2,
+  // 6.80 / 4.21 at m = 8; 2,048 x 12,288: 5.09 / 4.84 and 7.01 / 5.43;
+  // 1,024 x 16,384: 5.79 / 4.64 and 8.34 / 6.37), and 4,096 x 12,288 from
+  // m = 5 (6.66 / 6.59 at m = 5, 7.42 / 6.85 at m = 8; 5.38 / 6.02 at m = 2).
+  // 4,096 x 16,384 stays unsplit (9.21 / 9.94 at m = 8). Slices of 12, 24 and
+  // 24 units for n <= 1,024, <= 2,048 and beyond. One activation row, K of
+  // one 4,096-column slice and everything else run unsplit.
+  if (!fast || m == 1 || units <= 16 || k > kSplitMaxK)
+    return launch_ternary_gemm_small(packed, scale, n, k, x, m, y, stream);
+  if (n <= 1024) return launch_mfma_split<12, 1, 1>(packed, scale, n, k, x, m, y, ws, ws_bytes, stream);
+  if (n <= 2048) return launch_mfma_split<12, 1, 2>(packed, scale, n, k, x, m, y, ws, ws_bytes, stream);
+  if (n <= 4096 && units <= 48 && m >= 5)
+    return launch_mfma_split<8, 2, 3>(packed, scale, n, k, x, m, y, ws, ws_bytes, stream);
+  return launch_ternary_gemm_small(packed, scale, n, k, x, m, y, stream);
+}
 
 hipError_t launch_ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
                                const uint16_t* x, float* y, hipStream_t stream) {
@@ -503,7 +576,7 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
     return hipGetLastError();
   }
   const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
-  if (fast && units <= 48) {
+  if (fast && units <= 64) {
     // Launch shapes from graph-timed sweeps on MI355X at M = 2..8, clocks
     // settled, each shape timed in both orders. More tiles per workgroup
     // (each activation column reused by more rows) beat more waves down to
@@ -524,12 +597,14 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
       else launch_mfma_cfg<8, 1, 2>(packed, scale, n, k, x, m, y, stream);
     } else if (units <= 32) {
       launch_mfma_cfg<8, 1, 4>(packed, scale, n, k, x, m, y, stream);
-    } else if (m == 2) {
+    } else if (units <= 48 && m == 2) {
       launch_mfma_mp<8, 1, 6, 2>(packed, scale, n, k, x, m, y, stream);
-    } else if (m <= 4) {
+    } else if (units <= 48 && m <= 4) {
       launch_mfma_mp<8, 1, 6, 4>(packed, scale, n, k, x, m, y, stream);
-    } else {
+    } else if (units <= 48) {
       launch_mfma_mp<12, 1, 4, 8>(packed, scale, n, k, x, m, y, stream);
+    } else {
+      launch_mfma_cfg<8, 1, 8>(packed, scale, n, k, x, m, y, stream);  // K <= 16,384
     }
     return hipGetLastError();
   }

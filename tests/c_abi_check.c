@@ -49,6 +49,13 @@ int main(void) {
   expect("gemv packed misaligned", ternary_gemv((const uint32_t*)(base + 4), scale, 8, 64, x, y, 0), PBG_ERR_ALIGN);
   expect("small m = 0", ternary_gemm_small(packed, scale, 8, 64, x, 0, y, 0), PBG_ERR_SHAPE);
   expect("small m = 9", ternary_gemm_small(packed, scale, 8, 64, x, PBG_MAX_M + 1, y, 0), PBG_ERR_SHAPE);
+  expect("splitk workspace bytes", pbg_splitk_workspace_bytes(4096, 12288), 8 * 8 * (4096 + 64));
+  expect("splitk null workspace", ternary_gemm_splitk(packed, scale, 8, 64, x, 1, y, NULL, 1 << 20, 0), PBG_ERR_NULL);
+  expect("splitk workspace misaligned",
+         ternary_gemm_splitk(packed, scale, 8, 64, x, 1, y, (void*)(base + 0x9010), 1 << 20, 0), PBG_ERR_ALIGN);
+  expect("splitk workspace too small",
+         ternary_gemm_splitk(packed, scale, 4096, 12288, x, 8, y, (void*)(base + 0x9000), 1024, 0),
+         PBG_ERR_WORKSPACE);
   expect("head null y", int8_head_gemv(w, scale, 8, 64, x, 1, NULL, 0), PBG_ERR_NULL);
   expect("head w misaligned", int8_head_gemv(w + 8, scale, 8, 64, x, 1, y, 0), PBG_ERR_ALIGN);
   expect("argmax keys misaligned", int8_head_argmax(w, scale, 8, 64, x, 1, (uint64_t*)(base + 0x5004), token,

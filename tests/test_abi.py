@@ -44,12 +44,17 @@ def test_exports_every_header_function():
 
 def test_helpers():
     lib = binding.lib()
-    assert lib.pbg_abi_version() == 1
+    assert lib.pbg_abi_version() == 2
     for k, w in [(1, 4), (64, 4), (65, 8), (4096, 256), (12288, 768), (0, 0), (-5, 0)]:
         assert lib.pbg_words_per_row(k) == w
-    for code in range(-5, 1):
+    for code in range(-6, 1):
         assert lib.pbg_strerror(code)
     assert lib.pbg_strerror(-99) == b"unknown error code"
+    # split-K workspace: one 8-byte accumulator per output, at most 8 activation rows, row blocks
+    # of at most 64 rows; 0 for an invalid shape
+    assert lib.pbg_splitk_workspace_bytes(4096, 12288) == 8 * 8 * (4096 + 64)
+    assert lib.pbg_splitk_workspace_bytes(8, 4096) == 8 * 8 * 72
+    assert lib.pbg_splitk_workspace_bytes(0, 4096) == 0 and lib.pbg_splitk_workspace_bytes(8, 0) == 0
 
 
 @no_gpu_only
@@ -159,3 +164,27 @@ def test_stream_read_validation():
         assert lib.pbg_stream_read(GOOD, nbytes, GOOD, None) == -2
     assert lib.pbg_stream_read(GOOD + 8, 1024, GOOD, None) == -3
     assert lib.pbg_stream_read(GOOD, 1024, GOOD + 2, None) == -3
+
+
+@no_gpu_only
+def test_splitk_validation():
+    lib = binding.lib()
+    need = lib.pbg_splitk_workspace_bytes(4096, 12288)
+    assert lib.ternary_gemm_splitk(GOOD, GOOD, 4096, 12288, GOOD, 8, GOOD, None, need, None) == -1
+    assert lib.ternary_gemm_splitk(None, GOOD, 4096, 12288, GOOD, 8, GOOD, GOOD, need, None) == -1
+    for n, k, m in ((0, 12288, 1), (4096, 0, 1), (4096, 12288, 0), (4096, 12288, 9)):
+        assert lib.ternary_gemm_splitk(GOOD, GOOD, n, k, GOOD, m, GOOD, GOOD, need, None) == -2
+    assert lib.ternary_gemm_splitk(GOOD + 4, GOOD, 4096, 12288, GOOD, 8, GOOD, GOOD, need, None) == -3
+    assert lib.ternary_gemm_splitk(GOOD, GOOD, 4096, 12288, GOOD, 8, GOOD, GOOD + 128, need, None) == -3
+    assert lib.ternary_gemm_splitk(GOOD, GOOD, 4096, 12288, GOOD, 8, GOOD, GOOD, need - 1, None) == -6
+
+
+@no_gpu_only
+def test_noalloc_argmax_validation():
+    lib = binding.lib()
+    assert lib.int8_head_argmax_noalloc(None, GOOD, 4, 64, GOOD, 1, GOOD, None, None) == -1
+    assert lib.int8_head_argmax_noalloc(GOOD, GOOD, 4, 64, GOOD, 1, None, None, None) == -1
+    for n, k, m in ((0, 64, 1), (4, 0, 1), (4, 64, 0), (4, 64, 9)):
+        assert lib.int8_head_argmax_noalloc(GOOD, GOOD, n, k, GOOD, m, GOOD, None, None) == -2
+    assert lib.int8_head_argmax_noalloc(GOOD + 8, GOOD, 4, 64, GOOD, 1, GOOD, None, None) == -3
+    assert lib.int8_head_argmax_noalloc(GOOD, GOOD, 4, 64, GOOD, 1, GOOD + 2, None, None) == -3

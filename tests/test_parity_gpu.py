@@ -237,7 +237,7 @@ def test_gemv_full_size_sampled(pbg):
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(5, 16), (17, 65), (40, 4096), (21, 8200), (64, 12288), (8200, 4096),
                                  (1000, 12288), (3000, 4096), (100, 6000), (2100, 12280), (6144, 4096),
-                                 (700, 8192)])
+                                 (700, 8192), (300, 16384), (70, 13000)])
 def test_small_m_exact_probe(pbg, m, n, k):
     say(f"small-m exact m={m} n={n} k={k}")
     codes = synth.ternary_codes(8000 + n + k, n, k)
