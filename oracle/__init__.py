@@ -53,6 +53,20 @@ multiples of 2**-24, so with |x| < 2**9 and K < 2**20 every partial sum is an
 integer multiple of 2**-24 below 2**53 * 2**-24 and the fp64 sum is exact in
 any order; the only rounding is the final multiply by the scale.
 
+The 3-bit variant (five-level codes). The page sizes the shipped coded lane
+at exactly 3 bits per weight ("Where the bytes live") and splits its codes into
+zero, plus and minus ("Inside the coded lane"); this project reads the third
+bit as a magnitude: codes c in {-2, -1, 0, +1, +2}, y_r = s_r * sum_j c_rj x_j.
+Its layout, in words (once, here):
+  a row of K codes is padded with zero codes to K128 = 128 * ceil(K / 128) and
+  holds 12 * ceil(K / 128) words: first the sign/nonzero plane, K128 / 16
+  words in exactly the 2-bit layout above (a code of magnitude 2 is written
+  there like one of magnitude 1), then the magnitude plane, K128 / 32 words:
+  magnitude word q covers codes 32q .. 32q + 31, and code 32q + j, with
+  j = 16 i + 2 t + h (i = 0, 1; t = 0..7; h = 0, 1), sits at bit 16 h + 8 i + t,
+  set exactly when |c| = 2. A magnitude bit without its nonzero bit is
+  rejected on unpacking, like a sign bit without it.
+
 Parity pins: see tests/test_oracle.py (exhaustive single-word round trip,
 hand-written format words, the fp16 reading of the layout, brute force
 over all ternary rows for K <= 8 against exact rational sums, closed forms,
@@ -273,3 +287,122 @@ def ffn_swiglu(gate_packed: np.ndarray, gate_scale: np.ndarray, up_packed: np.nd
     h = (silu(g) * u).astype(np.float16)
     y = ternary_gemm_small(down_packed, down_scale, d_ff, h)
     return h, y
+
+
+# --------------------------------------------------------------------------
+# The 3-bit variant: five-level codes as a sign/nonzero plane (the 2-bit
+# layout) followed by a magnitude plane.
+# --------------------------------------------------------------------------
+CODES_PER_MAG_WORD = 32
+
+
+def words_per_row3(k: int) -> int:
+    """Words per 3-bit row: 12 * ceil(k / 128) (3 bits per code, 128-code groups)."""
+    if k <= 0:
+        raise ValueError("k must be positive")
+    return 12 * math.ceil(k / 128)
+
+
+def mag_bit_position(j: int) -> int:
+    """Bit of code j (0..31) inside its magnitude word."""
+    if not 0 <= j < CODES_PER_MAG_WORD:
+        raise ValueError("code index within a magnitude word is 0..31")
+    i, rest = divmod(j, 16)
+    t, h = divmod(rest, 2)
+    return 16 * h + 8 * i + t
+
+
+def count_codes3(codes: np.ndarray) -> np.ndarray:
+    """[n(-2), n(-1), n(0), n(+1), n(+2), n_invalid] over a code tensor (int64)."""
+    c = np.asarray(codes)
+    counts = [int(np.count_nonzero(c == v)) for v in (-2, -1, 0, 1, 2)]
+    return np.array(counts + [c.size - sum(counts)], dtype=np.int64)
+
+
+def pack3(codes: np.ndarray):
+    """Pack int8 codes [n, k] with values -2..+2 into the 3-bit layout.
+
+    Returns (packed uint32 [n, words_per_row3(k)], row_sum int32 [n],
+    counts int64[5] of -2, -1, 0, +1, +2). Raises ValueError on any other value.
+    """
+    codes = np.asarray(codes)
+    if codes.ndim != 2 or codes.dtype != np.int8:
+        raise ValueError("codes must be a 2-D int8 array")
+    n, k = codes.shape
+    stats = count_codes3(codes)
+    if stats[5] != 0:
+        raise ValueError(f"{stats[5]} codes outside -2..+2")
+    k128 = 128 * math.ceil(k / 128)
+    padded = np.zeros((n, k128), dtype=np.int8)
+    padded[:, :k] = codes
+    # sign/nonzero plane: the 2-bit layout of sign(c) (magnitude 2 written as 1)
+    sign_nz = np.sign(padded).astype(np.int8)
+    plane2 = np.zeros((n, k128 // CODES_PER_WORD), dtype=np.uint32)
+    grouped = sign_nz.reshape(n, -1, CODES_PER_WORD)
+    for j in range(CODES_PER_WORD):
+        nz_bit, sign_bit = bit_positions(j)
+        c = grouped[:, :, j]
+        plane2 |= (c != 0).astype(np.uint32) << np.uint32(nz_bit)
+        plane2 |= (c < 0).astype(np.uint32) << np.uint32(sign_bit)
+    # magnitude plane
+    plane_m = np.zeros((n, k128 // CODES_PER_MAG_WORD), dtype=np.uint32)
+    big = (np.abs(padded) == 2).reshape(n, -1, CODES_PER_MAG_WORD)
+    for j in range(CODES_PER_MAG_WORD):
+        plane_m |= big[:, :, j].astype(np.uint32) << np.uint32(mag_bit_position(j))
+    packed = np.concatenate([plane2, plane_m], axis=1)
+    assert packed.shape[1] == words_per_row3(k)
+    row_sum = codes.sum(axis=1, dtype=np.int64).astype(np.int32)
+    return packed, row_sum, stats[:5].copy()
+
+
+def unpack3(packed: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of pack3: uint32 [n, words_per_row3(k)] -> int8 codes [n, k].
+
+    Raises ValueError on a sign or magnitude bit without its nonzero bit, on a
+    row length that does not match k, or on a nonzero padding code.
+    """
+    packed = np.asarray(packed)
+    if packed.ndim != 2 or packed.dtype != np.uint32:
+        raise ValueError("packed must be a 2-D uint32 array")
+    n, w = packed.shape
+    if w != words_per_row3(k):
+        raise ValueError(f"row holds {w} words, k={k} needs {words_per_row3(k)}")
+    k128 = 128 * math.ceil(k / 128)
+    w2 = k128 // CODES_PER_WORD
+    # the sign/nonzero plane is the 2-bit layout; unpack() checks its fields
+    ternary = unpack(packed[:, :w2], w2 * CODES_PER_WORD)
+    plane_m = packed[:, w2:]
+    big = np.zeros((n, plane_m.shape[1], CODES_PER_MAG_WORD), dtype=bool)
+    for j in range(CODES_PER_MAG_WORD):
+        big[:, :, j] = ((plane_m >> np.uint32(mag_bit_position(j))) & np.uint32(1)).astype(bool)
+    big = big.reshape(n, k128)
+    if np.any(big & (ternary == 0)):
+        raise ValueError("magnitude bit set on a zero code")
+    codes = (ternary.astype(np.int16) * np.where(big, 2, 1)).astype(np.int8)
+    if np.any(codes[:, k:]):
+        raise ValueError("nonzero padding code")
+    return codes[:, :k].copy()
+
+
+def ternary3_gemm_small(packed: np.ndarray, scale: np.ndarray, k: int, x: np.ndarray,
+                        row_block: int = 16384) -> np.ndarray:
+    """Y[m, r] = s_r * sum_j c_rj * X[m, j] in fp64 for five-level codes."""
+    xs = _as_rows(x, k)
+    scale = np.asarray(scale)
+    if scale.dtype != np.float32 or scale.shape != (packed.shape[0],):
+        raise ValueError("scale must be fp32 [n]")
+    n = packed.shape[0]
+    y = np.empty((xs.shape[0], n), dtype=np.float64)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        c = unpack3(packed[r0:r1], k).astype(np.float64)
+        y[:, r0:r1] = (xs @ c.T) * scale[r0:r1].astype(np.float64)[None, :]
+    return y
+
+
+def ternary3_gemv(packed: np.ndarray, scale: np.ndarray, k: int, x: np.ndarray) -> np.ndarray:
+    """y_r = s_r * sum_j c_rj * x_j in fp64 (one activation row) for five-level codes."""
+    x = np.asarray(x)
+    if x.ndim != 1:
+        raise ValueError("ternary3_gemv takes one activation row")
+    return ternary3_gemm_small(packed, scale, k, x[None, :])[0]

@@ -117,6 +117,26 @@ def ternary_codes(seed: int, n: int, k: int, dist: CodeDist = GLOBAL_DIST) -> np
     return codes
 
 
+# Five-level codes of the 3-bit variant: the page gives only the split into
+# zero, plus and minus ("Inside the coded lane"); the share of magnitude 2
+# among nonzero codes is this project's choice (a quarter). One uniform draw
+# u per code: 0 if u < p0; +2 if u < p0 + P_BIG * p+, +1 if u < p0 + p+;
+# -2 if u < p0 + p+ + P_BIG * p-, else -1.
+P_BIG = 0.25
+
+
+def ternary3_codes(seed: int, n: int, k: int, dist: CodeDist = GLOBAL_DIST, p_big: float = P_BIG) -> np.ndarray:
+    """int8 five-level codes [n, k] (-2..+2) by the thresholds above."""
+    u = _rng(seed).random((n, k))
+    p0, pp = dist.p_zero, dist.p_plus
+    codes = np.full((n, k), -1, dtype=np.int8)
+    codes[u < p0 + pp + p_big * dist.p_minus] = -2
+    codes[u < p0 + pp] = 1
+    codes[u < p0 + p_big * pp] = 2
+    codes[u < p0] = 0
+    return codes
+
+
 def row_scales(seed: int, n: int, lo: float = 0.01, hi: float = 0.05) -> np.ndarray:
     """fp32 per-row scales ~ U[lo, hi)."""
     return _rng(seed + SEED_SCALE_OFFSET).uniform(lo, hi, size=n).astype(np.float32)
@@ -172,6 +192,33 @@ def ternary_codes_device(seed: int, n: int, k: int, dist: CodeDist, device, row_
         out[r0:r1] = c
         del u, c
     return out
+
+
+def ternary3_codes_device(seed: int, n: int, k: int, dist: CodeDist, device, p_big: float = P_BIG,
+                          row_block: int = 4096):
+    """int8 five-level codes [n, k] on ``device``; same thresholds as ternary3_codes."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty((n, k), dtype=torch.int8, device=device)
+    p0, pp = dist.p_zero, dist.p_plus
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        u = torch.rand((r1 - r0, k), generator=g, device=device)
+        c = torch.full_like(u, -1, dtype=torch.int8)
+        c[u < p0 + pp + p_big * dist.p_minus] = -2
+        c[u < p0 + pp] = 1
+        c[u < p0 + p_big * pp] = 2
+        c[u < p0] = 0
+        out[r0:r1] = c
+        del u, c
+    return out
+
+
+def words3_bytes(n: int, k: int) -> int:
+    """Bytes of one packed 3-bit tensor: rows of 12*ceil(k/128) uint32 words."""
+    return n * 4 * (12 * math.ceil(k / 128))
 
 
 def head_weights_device(seed: int, n: int, k: int, device, row_block: int = 16384):

@@ -62,6 +62,31 @@ def read_format_words():
     return rows
 
 
+def read_format3_words():
+    """Rows of tests/golden/format3_words.txt as (k, codes int8 [k], words uint32).
+
+    Codes may be written "a*n" for n copies of a."""
+    rows = []
+    with open(os.path.join(GOLDEN, "format3_words.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k_s, codes_s, words_s = (p.strip() for p in line.split("|"))
+            vals = []
+            for item in codes_s.split(","):
+                if "*" in item:
+                    v, cnt = item.split("*")
+                    vals += [int(v)] * int(cnt)
+                else:
+                    vals.append(int(item))
+            codes = np.array(vals, dtype=np.int8)
+            words = np.array([int(v, 16) for v in words_s.split()], dtype=np.uint32)
+            assert codes.size == int(k_s)
+            rows.append((int(k_s), codes, words))
+    return rows
+
+
 def read_key_values(name):
     out = {}
     with open(os.path.join(GOLDEN, name)) as f:

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import read_format_words, read_key_values
+from helpers import read_format3_words, read_format_words, read_key_values
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -460,3 +460,183 @@ def test_ffn_rows_independent():
     for m in range(3):
         h1, y1 = oracle.ffn_swiglu(g, sg, u, su, d, sd, d_model, x[m])
         assert np.array_equal(h1[0], h[m]) and np.array_equal(y1[0], y[m])
+
+
+# --------------------------------------------------------------------------
+# The 3-bit variant (five-level codes: sign/nonzero plane + magnitude plane)
+# --------------------------------------------------------------------------
+def test_words_per_row3():
+    assert oracle.words_per_row3(1) == 12
+    assert oracle.words_per_row3(128) == 12
+    assert oracle.words_per_row3(129) == 24
+    assert oracle.words_per_row3(4096) == 384  # 1,536 bytes: 3 bits per code
+    assert oracle.words_per_row3(12288) == 1152
+    with pytest.raises(ValueError):
+        oracle.words_per_row3(0)
+
+
+def test_mag_bit_positions_cover_word_once():
+    assert sorted(oracle.mag_bit_position(j) for j in range(32)) == list(range(32))
+
+
+@pytest.mark.parametrize("case", range(len(read_format3_words())))
+def test_golden_words3(case):
+    k, codes, words = read_format3_words()[case]
+    packed, row_sum, counts = oracle.pack3(codes[None, :])
+    assert [f"{v:08X}" for v in packed[0]] == [f"{v:08X}" for v in words]
+    assert np.array_equal(oracle.unpack3(words[None, :], k)[0], codes)
+    assert row_sum[0] == int(codes.astype(np.int64).sum())
+    assert counts.tolist() == [int(np.count_nonzero(codes == v)) for v in (-2, -1, 0, 1, 2)]
+
+
+def test_page_bytes_per_layer_3bit():
+    """The 3-bit rows reproduce the shipped lane's printed size exactly:
+    72,351,744 bytes per layer and 2,605 MB for 36 layers."""
+    g = read_key_values("neutrino_geometry.txt")
+    layer = sum(4 * n * oracle.words_per_row3(k) for n, k in synth.SHAPES.values())
+    assert layer == g["shipped_coded_bytes_per_layer"] == 72_351_744
+    assert round(g["layers"] * layer / 1e6) == 2605
+
+
+def test_fp16_reading_of_five_level_fields():
+    """sign at bit 15, nonzero at 14, magnitude at 10, read as fp16, is 2c."""
+    for c in (-2, -1, 0, 1, 2):
+        bits = (int(c < 0) << 15) | (int(c != 0) << 14) | (int(abs(c) == 2) << 10)
+        assert float(np.array([bits], dtype=np.uint16).view(np.float16)[0]) == 2.0 * c
+
+
+def test_magnitude_shift_recipe():
+    """The decode recipe the layout was chosen for: with M = m1:m0 the two
+    magnitude words of a 64-code chunk, M << (10 - t) holds pair t of sign/
+    nonzero word 0 at bits 10 and 26 of its low half and of word 2 in its
+    high half; M shifted left by 2 - t (right by t - 2) does so for words 1
+    and 3. Checked on random five-level codes against unpack3."""
+    codes = synth.ternary3_codes(71, 32, 64)
+    packed, _, _ = oracle.pack3(codes)
+    c = oracle.unpack3(packed, 64)
+    # k = 64 pads to 128 codes: sign/nonzero words 0..7, magnitude words 8..11; the
+    # chunk of codes 0..63 is sign/nonzero words 0..3 with magnitude words 8, 9
+    mags = packed[:, 8:10].astype(np.uint64)
+    big = np.abs(c) == 2
+    M = mags[:, 0] | (mags[:, 1] << np.uint64(32))
+    mask = np.uint64(0xFFFFFFFFFFFFFFFF)
+    for t in range(8):
+        a = (M << np.uint64(10 - t)) & mask
+        b = ((M << np.uint64(2 - t)) if t <= 2 else (M >> np.uint64(t - 2))) & mask
+        for word, src, half in ((0, a, 0), (2, a, 1), (1, b, 0), (3, b, 1)):
+            v = (src >> np.uint64(32 * half)) & np.uint64(0xFFFFFFFF)
+            lo = ((v >> np.uint64(10)) & np.uint64(1)).astype(bool)
+            hi = ((v >> np.uint64(26)) & np.uint64(1)).astype(bool)
+            assert np.array_equal(lo, big[:, 16 * word + 2 * t]), (t, word)
+            assert np.array_equal(hi, big[:, 16 * word + 2 * t + 1]), (t, word)
+
+
+def test_round_trip3_single_codes_and_injective():
+    """Every value at every position of a 128-code group (and past it) packs
+    to its own bits and unpacks back; distinct rows pack to distinct words."""
+    rows = []
+    for j in list(range(128)) + [128, 200, 255]:
+        for v in (-2, -1, 1, 2):
+            r = np.zeros(256, dtype=np.int8)
+            r[j] = v
+            rows.append(r)
+    codes = np.stack(rows)
+    packed, _, _ = oracle.pack3(codes)
+    assert np.array_equal(oracle.unpack3(packed, 256), codes)
+    assert len({p.tobytes() for p in packed}) == len(rows)
+    # each single code sets 1 (|c| = 1, +), 2 (sign) or 3 (|c| = 2) bits
+    bits = np.array([sum(bin(int(w)).count("1") for w in p) for p in packed])
+    expect = np.array([{-2: 3, -1: 2, 1: 1, 2: 2}[int(r[r != 0][0])] for r in codes])
+    assert np.array_equal(bits, expect)
+
+
+def test_round_trip3_exhaustive_six_positions():
+    """All 5^6 value combinations at six positions spread over both halves,
+    several pairs and both magnitude-word halves round-trip, injectively."""
+    pos = [0, 1, 17, 30, 33, 127]
+    vals = np.array(list(itertools.product((-2, -1, 0, 1, 2), repeat=len(pos))), dtype=np.int8)
+    codes = np.zeros((vals.shape[0], 128), dtype=np.int8)
+    codes[:, pos] = vals
+    packed, row_sum, counts = oracle.pack3(codes)
+    assert np.array_equal(oracle.unpack3(packed, 128), codes)
+    assert len({p.tobytes() for p in packed}) == vals.shape[0]
+    assert np.array_equal(row_sum, vals.astype(np.int64).sum(1))
+    assert counts.sum() == codes.size
+
+
+def test_pack3_of_ternary_codes_is_the_2bit_layout():
+    """For codes in {-1, 0, +1} the sign/nonzero plane is the 2-bit layout and
+    the magnitude plane is zero; doubling the codes sets the magnitude plane to
+    the nonzero bits and doubles every output exactly."""
+    n, k = 40, 4096
+    c = synth.ternary_codes(72, n, k)
+    p3, rs3, counts3 = oracle.pack3(c)
+    p2, rs2, counts2 = oracle.pack(c)
+    assert np.array_equal(p3[:, :256], p2) and not np.any(p3[:, 256:])
+    assert np.array_equal(rs3, rs2) and counts3.tolist() == [0, counts2[0], counts2[1], counts2[2], 0]
+    s = synth.row_scales(73, n)
+    x = synth.activations(74, 1, k)[0]
+    y1 = oracle.ternary3_gemv(p3, s, k, x)
+    assert np.array_equal(y1, oracle.ternary_gemv(p2, s, k, x))
+    pd, _, _ = oracle.pack3((2 * c).astype(np.int8))
+    assert np.array_equal(pd[:, :256], p2)
+    nzmask = np.array([[int(any(c[r, 32 * q: 32 * q + 32] != 0)) for q in range(128)] for r in range(n)])
+    assert np.array_equal(pd[:, 256:] != 0, nzmask.astype(bool))
+    assert np.array_equal(oracle.ternary3_gemv(pd, s, k, x), 2.0 * y1)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_brute_force3_all_rows_exact(k):
+    """Every five-level row of length k against exact rational sums rounded once."""
+    rows = np.array(list(itertools.product((-2, -1, 0, 1, 2), repeat=k)), dtype=np.int8)
+    x = synth.activations(80 + k, 1, k)[0]
+    s = np.full(rows.shape[0], 0.03125, dtype=np.float32)
+    y = oracle.ternary3_gemv(oracle.pack3(rows)[0], s, k, x)
+    xf = [Fraction(float(v)) for v in x]
+    for r in range(rows.shape[0]):
+        exact = sum((int(c) * xv for c, xv in zip(rows[r], xf)), Fraction(0)) * Fraction(float(s[r]))
+        assert y[r] == float(exact)
+
+
+def test_fsum3_exact_large_k():
+    k, n = 12288, 6
+    codes = synth.ternary3_codes(81, n, k)
+    x = synth.activations(82, 1, k)[0]
+    s = synth.row_scales(83, n)
+    y = oracle.ternary3_gemv(oracle.pack3(codes)[0], s, k, x)
+    for r in range(n):
+        ref = math.fsum(float(c) * float(v) for c, v in zip(codes[r], x))
+        assert y[r] == float(s[r]) * ref
+
+
+def test_unpack3_rejects_noncanonical_and_padding():
+    codes = np.zeros((1, 40), dtype=np.int8)
+    codes[0, 3] = 2
+    p, _, _ = oracle.pack3(codes)
+    bad = p.copy()
+    bad[0, 8] |= np.uint32(1 << oracle.mag_bit_position(5))  # magnitude bit on a zero code
+    with pytest.raises(ValueError, match="magnitude"):
+        oracle.unpack3(bad, 40)
+    bad = p.copy()
+    bad[0, 0] |= np.uint32(1 << oracle.bit_positions(6)[1])  # sign bit without nonzero
+    with pytest.raises(ValueError):
+        oracle.unpack3(bad, 40)
+    bad = p.copy()
+    bad[0, 3] |= np.uint32(1 << oracle.bit_positions(0)[0])  # code 48 sits in the padding
+    with pytest.raises(ValueError, match="padding"):
+        oracle.unpack3(bad, 40)
+    with pytest.raises(ValueError):
+        oracle.pack3(np.array([[3, 0]], dtype=np.int8))
+    x = np.zeros(40, dtype=np.float16)
+    x[2] = np.inf
+    with pytest.raises(ValueError, match="finite"):
+        oracle.ternary3_gemv(p, np.ones(1, dtype=np.float32), 40, x)
+
+
+def test_row_sums_and_counts3():
+    codes = synth.ternary3_codes(84, 50, 1000)
+    _, row_sum, counts = oracle.pack3(codes)
+    assert np.array_equal(row_sum, codes.astype(np.int64).sum(1))
+    assert counts.sum() == codes.size
+    hist = np.bincount((codes.astype(np.int64) + 2).ravel(), minlength=5)
+    assert counts.tolist() == hist.tolist()
