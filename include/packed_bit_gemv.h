@@ -167,6 +167,53 @@ int ternary_gemm_splitk(const uint32_t* packed, const float* scale, int64_t n, i
                         int64_t m, float* y, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The 3-bit variant: five-level codes c in {-2, -1, 0, +1, +2}, 3 bits per
+ * code, the size of the shipped coded lane.
+ * Source: Neutrino-1 8B model page, "Where the bytes live" (the coded lane
+ * is 72,351,744 bytes per layer, exactly 3 bits per coded weight) and
+ * "Inside the coded lane" (codes split into zero, plus and minus). The page
+ * does not say what the third bit means; this library reads it as a
+ * magnitude (|c| = 2) and fixes its own layout:
+ *   - a row of k codes is padded with zero codes to K128 = 128 * ceil(k/128)
+ *     and holds pbg_words_per_row3(k) = 12 * ceil(k / 128) words;
+ *   - words [0, K128 / 16): the sign/nonzero plane, exactly the 2-bit layout
+ *     above for sign(c) (a code of magnitude 2 is written like one of 1);
+ *   - words [K128 / 16, 3 * K128 / 32): the magnitude plane; magnitude word q
+ *     holds codes 32q .. 32q + 31, code 32q + j with j = 16i + 2t + h
+ *     (i = 0, 1; t = 0..7; h = 0, 1) at bit 16h + 8i + t, set iff |c| = 2;
+ *     a magnitude bit is never set without its nonzero bit.
+ *   - per row: an fp32 scale and an int32 row sum sum_j c_rj.
+ */
+int64_t pbg_words_per_row3(int64_t k);
+
+/*
+ * pack_ternary3 - load-time encoding of one five-level linear; as
+ * pack_ternary, with
+ *   codes    [n][k] int8, values -2..+2 (any alignment)
+ *   packed   [n][pbg_words_per_row3(k)] uint32 out, 16-byte aligned
+ *   stats    [6] int64 out, device, 8-byte aligned: counts of -2, -1, 0, +1,
+ *            +2 and of invalid codes (zeroed by this call)
+ *   stats_host  NULL, or a host array of 6 int64 (then the call waits and
+ *            returns PBG_ERR_CODE if any code was invalid)
+ * An invalid code is counted and packed as 0 and adds nothing to row_sum.
+ */
+int pack_ternary3(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, int32_t* row_sum,
+                  int64_t* stats, int64_t* stats_host, hipStream_t stream);
+
+/*
+ * ternary3_gemv / ternary3_gemm_small - ternary_gemv and ternary_gemm_small
+ * for five-level packs: y[r] = scale[r] * sum_j c[r][j] * x[j] (m = 1), or
+ * Y[i][r] for 1 <= m <= 8 activation rows, each weight word read once.
+ *   packed  [n][pbg_words_per_row3(k)] uint32, 16-byte aligned
+ *   scale, x, y, m as the 2-bit calls
+ */
+int ternary3_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                  hipStream_t stream);
+
+int ternary3_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                        int64_t m, float* y, hipStream_t stream);
+
+/*
  * int8_head_gemv - Y[i][v] = scale[v] * sum_j w[v][j] * X[i][j] for the int8
  * output head, 1 <= m <= 8 activation rows.
  * Source: Neutrino-1 8B model page, "Where the bytes live" (untied int8

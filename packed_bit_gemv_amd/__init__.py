@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     int8_head_gemv,
     lib,
     pack_ternary,
+    pack_ternary3,
     splitk_workspace,
     stream_read,
     ternary_ffn_swiglu,
@@ -19,7 +20,10 @@ from .binding import (  # noqa: F401
     ternary_gemm_small,
     ternary_gemm_splitk,
     ternary_gemv,
+    ternary3_gemm_small,
+    ternary3_gemv,
     words_per_row,
+    words_per_row3,
 )
 
 __all__ = [
@@ -30,6 +34,7 @@ __all__ = [
     "int8_head_gemv",
     "lib",
     "pack_ternary",
+    "pack_ternary3",
     "splitk_workspace",
     "stream_read",
     "ternary_ffn_swiglu",
@@ -37,5 +42,8 @@ __all__ = [
     "ternary_gemm_small",
     "ternary_gemm_splitk",
     "ternary_gemv",
+    "ternary3_gemm_small",
+    "ternary3_gemv",
     "words_per_row",
+    "words_per_row3",
 ]

@@ -32,6 +32,10 @@ _SIGNATURES = {
     "pack_ternary": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "ternary_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "ternary_gemm_small": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "pbg_words_per_row3": (_c_i64, [_c_i64]),
+    "pack_ternary3": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "ternary3_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "ternary3_gemm_small": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "pbg_splitk_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
     "ternary_gemm_splitk": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _c_i64, _vp]),
     "int8_head_gemv": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
@@ -175,6 +179,86 @@ def ternary_gemm_small(packed: torch.Tensor, scale: torch.Tensor, k: int, x: tor
     rc = lib().ternary_gemm_small(packed.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, y.data_ptr(),
                                   _stream(packed))
     _check("ternary_gemm_small", rc)
+    return y
+
+
+def words_per_row3(k: int) -> int:
+    return int(lib().pbg_words_per_row3(int(k)))
+
+
+def pack_ternary3(codes: torch.Tensor, packed: torch.Tensor | None = None, row_sum: torch.Tensor | None = None,
+                  stats: torch.Tensor | None = None, check: bool = True):
+    """Pack five-level int8 codes [n, k] (-2..+2) on the GPU. Returns (packed, row_sum, stats).
+
+    stats holds the counts of -2, -1, 0, +1, +2 and of invalid codes. With check=True the call
+    waits for the stream and raises PbgError if any code is outside -2..+2.
+    """
+    _dev(codes, "codes", torch.int8)
+    if codes.dim() != 2:
+        raise ValueError("codes must be [n, k]")
+    n, k = codes.shape
+    dev = codes.device
+    if packed is None:
+        packed = torch.empty((n, words_per_row3(k)), dtype=torch.int32, device=dev)
+    if row_sum is None:
+        row_sum = torch.empty((n,), dtype=torch.int32, device=dev)
+    if stats is None:
+        stats = torch.empty((6,), dtype=torch.int64, device=dev)
+    _dev(packed, "packed", torch.int32)
+    _dev(row_sum, "row_sum", torch.int32)
+    _dev(stats, "stats", torch.int64)
+    if tuple(packed.shape) != (n, words_per_row3(k)) or tuple(row_sum.shape) != (n,) or stats.numel() != 6:
+        raise ValueError("output shapes do not match codes")
+    host = (ctypes.c_int64 * 6)() if check else None
+    rc = lib().pack_ternary3(codes.data_ptr(), n, k, packed.data_ptr(), row_sum.data_ptr(), stats.data_ptr(),
+                             ctypes.addressof(host) if host is not None else None, _stream(codes))
+    _check("pack_ternary3", rc)
+    return packed, row_sum, stats
+
+
+def _ternary3_args(packed, scale, k, x):
+    _dev(packed, "packed", torch.int32)
+    _dev(scale, "scale", torch.float32)
+    _dev(x, "x", torch.float16)
+    n = packed.shape[0]
+    if packed.dim() != 2 or packed.shape[1] != words_per_row3(k):
+        raise ValueError(f"packed must be [n, {words_per_row3(k)}] for k={k}")
+    if tuple(scale.shape) != (n,):
+        raise ValueError("scale must be [n]")
+    return n
+
+
+def ternary3_gemv(packed: torch.Tensor, scale: torch.Tensor, k: int, x: torch.Tensor,
+                  y: torch.Tensor | None = None) -> torch.Tensor:
+    """Five-level y[r] = scale[r] * sum_j c[r, j] * x[j]; x fp16 [k], y fp32 [n]."""
+    n = _ternary3_args(packed, scale, k, x)
+    if tuple(x.shape) != (k,):
+        raise ValueError(f"x must be [{k}]")
+    if y is None:
+        y = torch.empty((n,), dtype=torch.float32, device=packed.device)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != (n,):
+        raise ValueError("y must be [n]")
+    rc = lib().ternary3_gemv(packed.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), y.data_ptr(), _stream(packed))
+    _check("ternary3_gemv", rc)
+    return y
+
+
+def ternary3_gemm_small(packed: torch.Tensor, scale: torch.Tensor, k: int, x: torch.Tensor,
+                        y: torch.Tensor | None = None) -> torch.Tensor:
+    """Five-level Y[i, r] = scale[r] * sum_j c[r, j] * X[i, j]; X fp16 [m, k], m <= 8; Y fp32 [m, n]."""
+    n = _ternary3_args(packed, scale, k, x)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=packed.device)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != (m, n):
+        raise ValueError("y must be [m, n]")
+    rc = lib().ternary3_gemm_small(packed.data_ptr(), scale.data_ptr(), n, k, x.data_ptr(), m, y.data_ptr(),
+                                   _stream(packed))
+    _check("ternary3_gemm_small", rc)
     return y
 
 

@@ -70,6 +70,40 @@ int pack_ternary(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, in
   return stats_host[3] > 0 ? PBG_ERR_CODE : PBG_OK;
 }
 
+int64_t pbg_words_per_row3(int64_t k) { return pbg::words_per_row3(k); }
+
+int pack_ternary3(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, int32_t* row_sum, int64_t* stats,
+                  int64_t* stats_host, hipStream_t stream) {
+  if (!codes || !packed || !row_sum || !stats) return PBG_ERR_NULL;
+  if (bad_nk(n, k)) return PBG_ERR_SHAPE;
+  if (misaligned(packed, 16) || misaligned(row_sum, 4) || misaligned(stats, 8)) return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  int rc = finish(pbg::launch_pack3(codes, n, k, packed, row_sum, stats, stream));
+  if (rc != PBG_OK || !stats_host) return rc;
+  if (hipMemcpyAsync(stats_host, stats, 6 * sizeof(int64_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PBG_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PBG_ERR_HIP;
+  return stats_host[5] > 0 ? PBG_ERR_CODE : PBG_OK;
+}
+
+int ternary3_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                  hipStream_t stream) {
+  if (!packed || !scale || !x || !y) return PBG_ERR_NULL;
+  if (bad_nk(n, k)) return PBG_ERR_SHAPE;
+  if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_ternary3_gemv(packed, scale, n, k, x, y, stream));
+}
+
+int ternary3_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                        int64_t m, float* y, hipStream_t stream) {
+  if (!packed || !scale || !x || !y) return PBG_ERR_NULL;
+  if (bad_nk(n, k) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(packed, 16) || misaligned(scale, 4) || misaligned(x, 2) || misaligned(y, 4)) return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_ternary3_gemm_small(packed, scale, n, k, x, static_cast<int>(m), y, stream));
+}
+
 int ternary_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
                  hipStream_t stream) {
   if (!packed || !scale || !x || !y) return PBG_ERR_NULL;

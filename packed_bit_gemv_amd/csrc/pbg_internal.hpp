@@ -65,4 +65,14 @@ int64_t embedding_blocks(int64_t m, int64_t k);
 
 inline int64_t words_per_row(int64_t k) { return k <= 0 ? 0 : 4 * ((k + 63) / 64); }
 
+// The 3-bit variant: 12 words per 128 codes (sign/nonzero plane, then magnitude plane).
+inline int64_t words_per_row3(int64_t k) { return k <= 0 ? 0 : 12 * ((k + 127) / 128); }
+
+hipError_t launch_pack3(const int8_t* codes, int64_t n, int64_t k, uint32_t* packed, int32_t* row_sum,
+                        int64_t* stats, hipStream_t stream);
+hipError_t launch_ternary3_gemv(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                                float* y, hipStream_t stream);
+hipError_t launch_ternary3_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                      const uint16_t* x, int m, float* y, hipStream_t stream);
+
 }  // namespace pbg

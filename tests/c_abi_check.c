@@ -56,6 +56,11 @@ int main(void) {
   expect("splitk workspace too small",
          ternary_gemm_splitk(packed, scale, 4096, 12288, x, 8, y, (void*)(base + 0x9000), 1024, 0),
          PBG_ERR_WORKSPACE);
+  expect("words_per_row3(4096)", pbg_words_per_row3(4096), 384);
+  expect("pack3 null codes", pack_ternary3(NULL, 8, 64, (uint32_t*)base, (int32_t*)(base + 0x1000),
+                                            (int64_t*)(base + 0x2000), NULL, 0), PBG_ERR_NULL);
+  expect("gemv3 k = 0", ternary3_gemv(packed, scale, 8, 0, x, y, 0), PBG_ERR_SHAPE);
+  expect("gemm3 small m = 9", ternary3_gemm_small(packed, scale, 8, 64, x, PBG_MAX_M + 1, y, 0), PBG_ERR_SHAPE);
   expect("head null y", int8_head_gemv(w, scale, 8, 64, x, 1, NULL, 0), PBG_ERR_NULL);
   expect("head w misaligned", int8_head_gemv(w + 8, scale, 8, 64, x, 1, y, 0), PBG_ERR_ALIGN);
   expect("argmax keys misaligned", int8_head_argmax(w, scale, 8, 64, x, 1, (uint64_t*)(base + 0x5004), token,

@@ -33,6 +33,11 @@ def head_bound(w: np.ndarray, scale: np.ndarray, x: np.ndarray, row_block: int =
     return out
 
 
+def ternary3_bound(codes: np.ndarray, scale: np.ndarray, x: np.ndarray, row_block: int = 16384) -> np.ndarray:
+    """Per-element bound [m, n] for five-level outputs: 1e-3 * s_r * sum_j |c_rj| |x_j|."""
+    return head_bound(codes, scale, x, row_block)
+
+
 def assert_within(y, y_ref, bound, what=""):
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)

@@ -188,3 +188,19 @@ def test_noalloc_argmax_validation():
         assert lib.int8_head_argmax_noalloc(GOOD, GOOD, n, k, GOOD, m, GOOD, None, None) == -2
     assert lib.int8_head_argmax_noalloc(GOOD + 8, GOOD, 4, 64, GOOD, 1, GOOD, None, None) == -3
     assert lib.int8_head_argmax_noalloc(GOOD, GOOD, 4, 64, GOOD, 1, GOOD + 2, None, None) == -3
+
+
+@no_gpu_only
+def test_ternary3_validation():
+    lib = binding.lib()
+    assert lib.pbg_words_per_row3(1) == 12 and lib.pbg_words_per_row3(4096) == 384
+    assert lib.pbg_words_per_row3(129) == 24 and lib.pbg_words_per_row3(0) == 0
+    assert lib.pack_ternary3(None, 4, 64, GOOD, GOOD, GOOD, None, None) == -1
+    assert lib.pack_ternary3(GOOD, 0, 64, GOOD, GOOD, GOOD, None, None) == -2
+    assert lib.pack_ternary3(GOOD, 4, 64, GOOD + 4, GOOD, GOOD, None, None) == -3
+    assert lib.ternary3_gemv(GOOD, None, 4, 64, GOOD, GOOD, None) == -1
+    assert lib.ternary3_gemv(GOOD, GOOD, 4, 2 ** 24 + 1, GOOD, GOOD, None) == -2
+    assert lib.ternary3_gemv(GOOD + 8, GOOD, 4, 64, GOOD, GOOD, None) == -3
+    for m in (0, 9):
+        assert lib.ternary3_gemm_small(GOOD, GOOD, 4, 64, GOOD, m, GOOD, None) == -2
+    assert lib.ternary3_gemm_small(GOOD, GOOD, 4, 64, GOOD + 1, 2, GOOD, None) == -3
