@@ -50,6 +50,13 @@ __device__ __forceinline__ uint64_t mag_b(uint64_t m) {
 
 __device__ __forceinline__ uint32_t with_mag(uint32_t op2, uint32_t mag_src) { return (mag_src & kMagMask) | op2; }
 
+// Magnitude bits of pair t of sign/nonzero word i (0 or 1) of a magnitude
+// word, placed at bits 10 and 26 (bits 8i + t and 16 + 8i + t move there).
+__device__ __forceinline__ uint32_t mag_pair(uint32_t mw, int i, int t) {
+  const int s = 10 - 8 * i - t;
+  return (s >= 0 ? mw << s : mw >> -s) & kMagMask;
+}
+
 // Step T of a chunk: the four operands of pair T, each fed to its dot2.
 template <int T>
 __device__ __forceinline__ void chunk3_steps(uint64_t lo, uint64_t hi, uint64_t m, const uint32_t* xp, float& a) {
@@ -280,13 +287,6 @@ __global__ __launch_bounds__(G* kWave) void ternary3_gemv_kernel(const uint32_t*
   if (slot >= 0 && slot < R && row0 + slot < n) y[row0 + slot] = red * (sc * kCodeUnitInv);
 }
 
-// Magnitude bits of pair t of sign/nonzero word i (0 or 1) of a magnitude
-// word, placed at bits 10 and 26 (bits 8i + t and 16 + 8i + t move there).
-__device__ __forceinline__ uint32_t mag_pair(uint32_t mw, int i, int t) {
-  const int s = 10 - 8 * i - t;
-  return (s >= 0 ? mw << s : mw >> -s) & kMagMask;
-}
-
 // Any k and 2-byte-aligned x, 1 <= M <= 8 rows: a wave owns 4 rows and lane l
 // the sign/nonzero words l, l + 64, ... of each (16 codes) with their
 // magnitude bits; activations are loaded with element guards. Used when the
@@ -330,6 +330,156 @@ __global__ __launch_bounds__(4 * kWave) void ternary3_generic_kernel(const uint3
     const float r = wave_reduce4(acc[0][m], acc[1][m], acc[2][m], acc[3][m]);
     if (slot >= 0 && row0 + slot < n) y[m * n + row0 + slot] = r * (scale[row0 + slot] * kCodeUnitInv);
   }
+}
+
+// Magnitude bits of pair t of sign/nonzero word `word` (0..3) of a chunk, at
+// bits 10 and 26, from the chunk's magnitude words m0 (words 0, 1) and m1
+// (words 2, 3). Bits 8i + t and 16 + 8i + t of the word's magnitude word (i =
+// word & 1) move there with one 32-bit shift; word and t are compile-time
+// constants wherever this is inlined.
+__device__ __forceinline__ uint32_t mag_of(uint32_t m0, uint32_t m1, int word, int t) {
+  return mag_pair(word < 2 ? m0 : m1, word & 1, t);
+}
+
+// 2 <= M <= 8 on the matrix cores (k % 8 == 0, x 16-byte aligned): the 2-bit
+// small-M kernel of ternary.hip (ternary_gemm_mfma_kernel: 16-row tiles of
+// decoded codes as the A operand of v_mfma_f32_16x16x32_f16, activations as
+// B columns, whole-line x loads transposed through a per-wave LDS slice, SK
+// waves splitting the 256-column units of T tiles) with the magnitude bits
+// OR-ed into every A operand. Lane (i, g) loads, per unit, sign/nonzero chunk
+// 4u + g of its row (16 bytes) and that chunk's two magnitude words.
+template <int SK, int T, int UPW, int MP>
+__global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uint32_t* __restrict__ packed,
+                                                                        const float* __restrict__ scale, int64_t n,
+                                                                        int64_t k, int64_t chunks,
+                                                                        const uint16_t* __restrict__ x, int m,
+                                                                        float* __restrict__ y) {
+  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+  typedef float float4_t __attribute__((ext_vector_type(4)));
+  constexpr int kRows = 16 * T;
+  __shared__ float part[SK][kRows][8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int64_t groups = k / 8;
+  const int64_t row_words = 6 * chunks;
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+
+  constexpr int kOut = (kRows * 8 + SK * kWave - 1) / (SK * kWave);
+  float sc[kOut];
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    const int64_t r = row_base + (o < kRows * 8 ? o >> 3 : kRows - 1);
+    sc[e] = scale[r < n ? r : n - 1];
+  }
+
+  constexpr int kXLoads = MP / 2;
+  constexpr int kSlots = 33;  // 16-byte slots per row and unit, one of padding
+  __shared__ uint4 xs[SK][2][MP * kSlots];
+  const int xrow = li >> 3, xg8 = li & 7;
+  auto load_x = [&](int q, uint4 (&xr)[kXLoads]) {
+    const int64_t u = s + static_cast<int64_t>(SK) * q;
+#pragma unroll
+    for (int a = 0; a < kXLoads; ++a) {
+      const int row = 2 * a + xrow;
+      const int64_t gi = 32 * u + 8 * lg + xg8;
+      xr[a] = xg[row < m && gi < groups ? static_cast<int64_t>(row) * groups + gi : 0];
+    }
+  };
+  auto stage_x = [&](int q, const uint4 (&xr)[kXLoads]) {
+    const int64_t gi = 32 * (s + static_cast<int64_t>(SK) * q) + 8 * lg + xg8;
+#pragma unroll
+    for (int a = 0; a < kXLoads; ++a)
+      xs[s][q & 1][(2 * a + xrow) * kSlots + 8 * lg + xg8] = masked(xr[a], gi < groups);
+  };
+  auto load_w = [&](int q, uint4 (&wv)[T], uint2 (&mv)[T]) {
+    const int64_t c = 4 * (s + static_cast<int64_t>(SK) * q) + lg;
+    const int64_t cc = c < chunks ? c : chunks - 1;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t r = row_base + 16 * t + li;
+      const uint32_t* row = packed + (r < n ? r : n - 1) * row_words;
+      wv[t] = load_nt(reinterpret_cast<const uint4*>(row) + cc);
+      mv[t] = load_nt2(reinterpret_cast<const uint2*>(row + 4 * chunks) + cc);
+    }
+  };
+
+  float4_t d[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xr[kXLoads], wv[2][T];
+  uint2 mv[2][T];
+  load_x(0, xr);
+  load_w(0, wv[0], mv[0]);
+  stage_x(0, xr);
+  if (UPW > 1) {
+    load_x(1, xr);
+    load_w(1, wv[1], mv[1]);
+  }
+  const int brow = (li % MP) * kSlots + 8 * lg;
+#pragma unroll
+  for (int q = 0; q < UPW; ++q) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const half8_t b = __builtin_bit_cast(half8_t, xs[s][q & 1][brow + v]);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int word = v >> 1, h = v & 1;
+        const uint32_t wd = (&wv[q & 1][t].x)[word];
+        const uint32_t m0 = mv[q & 1][t].x, m1 = mv[q & 1][t].y;
+        const uint4 ap = make_uint4(code_pair(wd, 4 * h + 0) | mag_of(m0, m1, word, 4 * h + 0),
+                                    code_pair(wd, 4 * h + 1) | mag_of(m0, m1, word, 4 * h + 1),
+                                    code_pair(wd, 4 * h + 2) | mag_of(m0, m1, word, 4 * h + 2),
+                                    code_pair(wd, 4 * h + 3) | mag_of(m0, m1, word, 4 * h + 3));
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
+      }
+    }
+    if (q + 1 < UPW) {
+      stage_x(q + 1, xr);
+      if (q + 2 < UPW) {
+        load_x(q + 2, xr);
+        load_w(q + 2, wv[q & 1], mv[q & 1]);
+      }
+    }
+  }
+  if (li < 8) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[s][16 * t + 4 * lg + r][li] = d[t][r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = threadIdx.x + e * SK * kWave;
+    const int orow = o >> 3, ocol = o & 7;
+    const int64_t r = row_base + orow;
+    if (o < kRows * 8 && ocol < m && r < n) {
+      float sum = part[0][orow][ocol];
+#pragma unroll
+      for (int w = 1; w < SK; ++w) sum += part[w][orow][ocol];
+      y[static_cast<int64_t>(ocol) * n + r] = sum * (sc[e] * kCodeUnitInv);
+    }
+  }
+}
+
+template <int SK, int T, int UPW, int MP>
+void launch_mfma3_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, int64_t chunks,
+                     const uint16_t* x, int m, float* y, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
+  hipLaunchKernelGGL((ternary3_gemm_mfma_kernel<SK, T, UPW, MP>), grid, dim3(SK * kWave), 0, stream, packed, scale,
+                     n, k, chunks, x, m, y);
+}
+
+template <int SK, int T, int UPW>
+void launch_mfma3_cfg(const uint32_t* packed, const float* scale, int64_t n, int64_t k, int64_t chunks,
+                      const uint16_t* x, int m, float* y, hipStream_t stream) {
+  if (m <= 2) launch_mfma3_mp<SK, T, UPW, 2>(packed, scale, n, k, chunks, x, m, y, stream);
+  else if (m <= 4) launch_mfma3_mp<SK, T, UPW, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+  else launch_mfma3_mp<SK, T, UPW, 8>(packed, scale, n, k, chunks, x, m, y, stream);
 }
 
 template <int CPL, int G, int R>
@@ -396,6 +546,22 @@ hipError_t launch_ternary3_gemm_small(const uint32_t* packed, const float* scale
                                       const uint16_t* x, int m, float* y, hipStream_t stream) {
   if (m == 1) return launch_ternary3_gemv(packed, scale, n, k, x, y, stream);
   const int64_t chunks = words_per_row3(k) / 6;
+  const int64_t units = (chunks + 3) / 4;  // 256-column units
+  if (k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && units <= 64) {
+    // The 2-bit small-M launch shapes (ternary.hip), by rows and units.
+    if (units <= 16) {
+      if (n >= 8192) launch_mfma3_cfg<4, 3, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+      else if (n >= 5120) launch_mfma3_cfg<4, 2, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+      else launch_mfma3_cfg<8, 1, 2>(packed, scale, n, k, chunks, x, m, y, stream);
+    } else if (units <= 32) {
+      launch_mfma3_cfg<8, 1, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+    } else if (units <= 48) {
+      launch_mfma3_cfg<12, 1, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+    } else {
+      launch_mfma3_cfg<8, 1, 8>(packed, scale, n, k, chunks, x, m, y, stream);
+    }
+    return hipGetLastError();
+  }
   switch (m) {
     case 2: launch_generic3<2>(packed, scale, n, k, chunks, x, y, stream); break;
     case 3: launch_generic3<3>(packed, scale, n, k, chunks, x, y, stream); break;

@@ -139,7 +139,8 @@ def test_gemv3_exact_probe(pbg, n, k):
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
-@pytest.mark.parametrize("n,k", [(5, 16), (40, 4096), (33, 4100), (64, 12288), (700, 8192), (2100, 4096)])
+@pytest.mark.parametrize("n,k", [(5, 16), (40, 4096), (33, 4100), (64, 12288), (700, 8192), (2100, 4096),
+                                 (9000, 4096), (6000, 4096), (300, 16384), (77, 4000)])
 def test_gemm3_small_exact_probe(pbg, m, n, k):
     say(f"gemm3 exact m={m} n={n} k={k}")
     codes = synth.ternary3_codes(5500 + n + k, n, k)
