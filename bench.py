@@ -62,6 +62,11 @@ def ffn_block_bytes(d_model: int, d_ff: int, m: int = 1) -> int:
     return gate_up_bytes(d_ff, d_model, m) + ternary_bytes(d_model, d_ff, m)
 
 
+def ternary3_bytes(n: int, k: int, m: int = 1) -> int:
+    """Algorithmic bytes of one 3-bit call: packed rows + fp32 scales + fp16 x + fp32 y."""
+    return synth.words3_bytes(n, k) + 4 * n + 2 * m * k + 4 * m * n
+
+
 def head_bytes(n: int, k: int, m: int = 1) -> int:
     return n * k + 4 * n + 2 * m * k + 4 * m * n
 
@@ -560,6 +565,60 @@ def main():
         extra["verify_step_fused_m8_us"] = round(ms * 1e3, 1)
         extra["verify_step_fused_m8_GBs"] = round(vb / (ms * 1e-3) / 1e9, 1)
         del g, fused, yqkv_m, h_m, y_m
+
+        # the 3-bit lane (five-level codes, the shipped lane's 72,351,744 bytes
+        # of weights per layer): a pool of L layers of the 7 linears, per-linear
+        # launches, the read of their packed bytes, and whole layers at M = 1 and 8
+        pool3 = []
+        st6 = torch.empty(6, dtype=torch.int64, device=device)
+        for l in range(L):
+            lay = {}
+            for p in synth.PROJECTIONS:
+                n, k = synth.SHAPES[p]
+                seed = synth.tensor_seed(l, p)
+                codes = synth.ternary3_codes_device(seed, n, k, synth.code_dist(l, p), device)
+                lay[p] = (pbg.pack_ternary3(codes, stats=st6, check=False)[0], synth.row_scales_device(seed, n, device),
+                          n, k)
+                del codes
+            pool3.append(lay)
+        torch.cuda.synchronize()
+
+        def linear3(l, p, m=1):
+            packed, s, n, k = pool3[l][p]
+            if m == 1:
+                pbg.ternary3_gemv(packed, s, k, xs[k][0], ys[p][0])
+            else:
+                pbg.ternary3_gemm_small(packed, s, k, xs[k][:m], ys[p][:m])
+
+        lane3 = {"us_per_launch": {}, "GBs_per_launch": {}, "stream_read_us": {}}
+        for p in synth.PROJECTIONS:
+            n, k = synth.SHAPES[p]
+            g = capture(torch, lambda p=p: [linear3(l, p) for l in range(L)])
+            us = time_graphs(torch, [g], 5, 1) * 1e3 / L
+            lane3["us_per_launch"][p] = round(us, 3)
+            lane3["GBs_per_launch"][p] = round(ternary3_bytes(n, k) / (us * 1e-6) / 1e9, 1)
+            del g
+        for p in ("gate", "down", "q", "k"):
+            g = capture(torch, lambda p=p: [pbg.stream_read(pool3[l][p][0], sink) for l in range(L)])
+            lane3["stream_read_us"][p] = round(time_graphs(torch, [g], 5, 1) * 1e3 / L, 3)
+            del g
+        layer3_weights = sum(synth.words3_bytes(*synth.SHAPES[p]) for p in synth.PROJECTIONS)
+        lane3["layer_weight_bytes"] = layer3_weights
+        for m in (1, 8):
+            graphs = [capture(torch, lambda l=l, m=m: [linear3(l, p, m) for p in synth.PROJECTIONS])
+                      for l in range(L)]
+            ms = time_graphs(torch, graphs, K, W)
+            lb = sum(ternary3_bytes(*synth.SHAPES[p], m) for p in synth.PROJECTIONS)
+            lane3[f"layer_m{m}_us"] = round(ms * 1e3, 3)
+            lane3[f"layer_m{m}_GBs"] = round(lb / (ms * 1e-3) / 1e9, 1)
+            del graphs
+            g = capture(torch, lambda m=m: [linear3(l, p, m) for l in range(L) for p in synth.PROJECTIONS])
+            ms = time_graphs(torch, [g], 5, 1) / L
+            lane3[f"layer_m{m}_us_36_per_graph"] = round(ms * 1e3, 3)
+            lane3[f"layer_m{m}_GBs_36_per_graph"] = round(lb / (ms * 1e-3) / 1e9, 1)
+            del g
+        extra["lane3"] = lane3
+        del pool3
 
         # streaming-read ceiling at the gate byte count: torch copy over a pool
         nbytes = synth.words_bytes(*synth.SHAPES["gate"])

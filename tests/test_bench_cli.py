@@ -58,6 +58,14 @@ def test_ffn_block_bytes():
                                                                         + 4 * 4096))
 
 
+def test_lane3_bytes():
+    # the 3-bit rows of the seven linears are the shipped lane's 72,351,744 bytes per layer
+    weights = sum(synth.words3_bytes(*synth.SHAPES[p]) for p in synth.PROJECTIONS)
+    assert weights == 72_351_744
+    assert bench.ternary3_bytes(*synth.SHAPES["gate"]) == 12288 * 1536 + 4 * 12288 + 2 * 4096 + 4 * 12288
+    assert bench.ternary3_bytes(*synth.SHAPES["down"], 8) == 4096 * 4608 + 4 * 4096 + 8 * (2 * 12288 + 4 * 4096)
+
+
 def test_more_than_one_gpu_is_refused():
     proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                           text=True, timeout=300, cwd=ROOT)
