@@ -390,8 +390,8 @@ void launch_head_mfma(const int8_t* w, const float* scale, int64_t n, int64_t k,
 
 
 // 2 <= M <= 8 with k % 1024 == 0 and k <= 4096 (w and x 16-byte aligned).
-// Persistent: workgroup b converts a contiguous range of 16-row tiles, kPTiles
-// at a time (row blocks), and x is copied into LDS once per workgroup, by direct
+// Persistent: workgroup b converts row blocks b, b + grid, ... of kPTiles
+// 16-row tiles, and x is copied into LDS once per workgroup, by direct
 // global-to-LDS loads, in the order the MFMA B operand reads it: group q
 // (columns 8q .. 8q + 7) of row j sits at ((2 (q / 8) + q % 2) * 4 +
 // (q % 8) / 2) * M + j. Wave (tg, kq) owns tile tg and the contiguous K
@@ -435,30 +435,16 @@ __global__ __launch_bounds__(kPWaves* kWave) void int8_head_persist_kernel(const
   const int64_t chunks = k / 16;
   const int upw = static_cast<int>(k / (64 * kPQuarters));  // units per wave and row block
   const int nb = upw / kPBatch;                              // batches per row block
-  // Workgroup b owns the contiguous 16-row tiles [t0, t1), an equal share of
-  // all of them to within one tile, and walks them kPTiles at a time; the
-  // last row block may hold a single tile, whose second tile's waves then
-  // load nothing and write nothing.
-  const int64_t ntiles = (n + 15) / 16;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * ntiles / gridDim.x;
-  const int64_t t1 = (static_cast<int64_t>(blockIdx.x) + 1) * ntiles / gridDim.x;
-  const int my_rb = static_cast<int>((t1 - t0 + kPTiles - 1) / kPTiles);
+  const int64_t nrb = (n + kRows - 1) / kRows;
+  const int my_rb = static_cast<int>((nrb - blockIdx.x + gridDim.x - 1) / gridDim.x);
   const int total = my_rb * nb;
   const uint4* wq = reinterpret_cast<const uint4*>(w);
   const uint4* xg = reinterpret_cast<const uint4*>(x);
   const int o = threadIdx.x;  // output (row o / M, column o % M) of each row block
-  auto first_tile = [&](int i) { return t0 + static_cast<int64_t>(i) * kPTiles; };
-  auto out_row = [&](int i) { return first_tile(i) * 16 + o / M; };
-  auto out_ok = [&](int i) { return first_tile(i) + (o / M) / 16 < t1; };  // the row's tile is this workgroup's
+  auto out_row = [&](int i) { return (blockIdx.x + static_cast<int64_t>(i) * gridDim.x) * kRows + o / M; };
 
   auto load_batch = [&](int g, uint4 (&wv)[kPBatch]) {
-    const int64_t tile = first_tile(g / nb) + tg;  // wave-uniform
-    if (tile >= t1) {
-#pragma unroll
-      for (int c = 0; c < kPBatch; ++c) wv[c] = make_uint4(0u, 0u, 0u, 0u);
-      return;
-    }
-    const int64_t r = tile * 16 + li;
+    const int64_t r = (blockIdx.x + static_cast<int64_t>(g / nb) * gridDim.x) * kRows + tg * 16 + li;
     const uint4* row = wq + (r < n ? r : n - 1) * chunks;
     const int u0 = kq * upw + (g % nb) * kPBatch;
 #pragma unroll
@@ -504,7 +490,7 @@ __global__ __launch_bounds__(kPWaves* kWave) void int8_head_persist_kernel(const
     d = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     __syncthreads();
     const int64_t r = out_row(i);
-    if (o < kRows * M && r < n && out_ok(i)) {
+    if (o < kRows * M && r < n) {
       const int lr = o / M, ocol = o % M;
       float sum = part[p][lr / 16][0][lr % 16][ocol];
 #pragma unroll
