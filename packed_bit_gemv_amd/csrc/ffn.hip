@@ -6,10 +6,14 @@
 //   launch 2   y = down h (the M = 1 GEMV of ternary.hip)   -> y
 //
 // Launch 1 reads gate and up (same K, same x) in one pass and forms h in its
-// epilogue, so the gate and up outputs never reach memory. A single
-// persistent launch with a grid-wide barrier between the two phases was
-// measured slower on gfx950: the barrier, the exchange of h through memory
-// and the down decode after the barrier cost more than the second launch.
+// epilogue, so the gate and up outputs never reach memory. One launch for
+// the whole block was measured slower on gfx950 in two forms:
+// - A persistent grid with a grid-wide barrier: the barrier, the exchange of
+//   h through memory and the down decode after the barrier cost more than
+//   the second launch.
+// - Dataflow workgroups, with down waiting per slice of h on counters: even
+//   with the waits removed, the down reads finished no sooner than in their
+//   own launch, and the write-through handoff of h slowed the gate|up half.
 //
 // Work split of launch 1: a wave owns R consecutive row pairs (gate row r and
 // up row r) and reads 16-byte chunk `lane` (64 codes) of each; x is staged
