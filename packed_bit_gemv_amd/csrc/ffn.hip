@@ -127,8 +127,6 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
     const uint4* __restrict__ gate, const float* __restrict__ gate_scale, const uint4* __restrict__ up,
     const float* __restrict__ up_scale, int64_t d_model, int64_t d_ff, int64_t chunks, const uint16_t* __restrict__ x,
     int m, uint16_t* __restrict__ h) {
-  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-  typedef float float4_t __attribute__((ext_vector_type(4)));
   constexpr int kPairsWg = 8 * T;  // gate/up row pairs of the workgroup
   __shared__ float part[SK][16 * T][8];
   const int lane = threadIdx.x & (kWave - 1);
@@ -180,9 +178,9 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
     }
   };
 
-  float4_t d[T];
+  mfma_float4_t d[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < T; ++t) d[t] = mfma_float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   uint4 xr[kXLoads], wv[2][T];
   load_x(0, xr);
   load_w(0, wv[0]);
@@ -195,18 +193,8 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
 #pragma unroll
   for (int q = 0; q < UPW; ++q) {
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const half8_t b = __builtin_bit_cast(half8_t, xs[s][q & 1][brow + v]);
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
-        const int hh = v & 1;
-        const uint4 ap = make_uint4(code_pair(wd, 4 * hh + 0), code_pair(wd, 4 * hh + 1), code_pair(wd, 4 * hh + 2),
-                                    code_pair(wd, 4 * hh + 3));
-        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
-      }
-    }
+    mfma_unit_half<0, T>(wv[q & 1], &xs[s][q & 1][brow], d);
+    mfma_unit_half<1, T>(wv[q & 1], &xs[s][q & 1][brow], d);
     if (q + 1 < UPW) {
       stage_x(q + 1, xr);
       if (q + 2 < UPW) {

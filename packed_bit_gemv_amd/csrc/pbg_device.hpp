@@ -102,6 +102,49 @@ __device__ __forceinline__ void chunk_steps_m(uint64_t lo, uint64_t hi, const ui
   if constexpr (T < 7) chunk_steps_m<M, T + 1>(lo, hi, xp, a);
 }
 
+// Matrix-core A operands of half H (0 or 1) of a 16-byte chunk: a[w] holds
+// codes 8H .. 8H + 7 of word w (operands 4H .. 4H + 3) as eight fp16 2*c.
+// Each 64-bit shift serves two words, as in chunk_steps.
+template <int H>
+__device__ __forceinline__ void chunk_half_ops(const uint4& c, uint4 (&a)[4]) {
+  const uint64_t lo = static_cast<uint64_t>(c.y) << 32 | c.x;
+  const uint64_t hi = static_cast<uint64_t>(c.w) << 32 | c.z;
+  uint32_t o[4][4];
+  pair_ops<4 * H + 0>(lo, o[0][0], o[1][0]);
+  pair_ops<4 * H + 0>(hi, o[2][0], o[3][0]);
+  pair_ops<4 * H + 1>(lo, o[0][1], o[1][1]);
+  pair_ops<4 * H + 1>(hi, o[2][1], o[3][1]);
+  pair_ops<4 * H + 2>(lo, o[0][2], o[1][2]);
+  pair_ops<4 * H + 2>(hi, o[2][2], o[3][2]);
+  pair_ops<4 * H + 3>(lo, o[0][3], o[1][3]);
+  pair_ops<4 * H + 3>(hi, o[2][3], o[3][3]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) a[w] = make_uint4(o[w][0], o[w][1], o[w][2], o[w][3]);
+}
+
+typedef _Float16 mfma_half8_t __attribute__((ext_vector_type(8)));
+typedef float mfma_float4_t __attribute__((ext_vector_type(4)));
+
+// Half H of one 256-column unit on the matrix cores, for T 16-row tiles:
+// tile t's lane chunk wv[t], and xb the lane's 8 B slots of the unit, where
+// slot v holds the activation columns of codes 8 (v % 2) .. 8 (v % 2) + 7 of
+// word v / 2. Word w's half H is multiplied by slot 2w + H; the 4 slots are
+// read once for all T tiles.
+template <int H, int T>
+__device__ __forceinline__ void mfma_unit_half(const uint4 (&wv)[T], const uint4* xb, mfma_float4_t (&d)[T]) {
+  mfma_half8_t b[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) b[w] = __builtin_bit_cast(mfma_half8_t, xb[2 * w + H]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    uint4 a[4];
+    chunk_half_ops<H>(wv[t], a);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mfma_half8_t, a[w]), b[w], d[t], 0, 0, 0);
+  }
+}
+
 // acc[m] += the chunk's sum against activation row m.
 template <int M>
 __device__ __forceinline__ void chunk_dot_m(const uint4& w, const uint32_t (*xp)[32], float* acc) {

@@ -310,8 +310,6 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
                                                                        int64_t n, int64_t k, int64_t chunks,
                                                                        const uint16_t* __restrict__ x, int m,
                                                                        float* __restrict__ y, SplitK sp) {
-  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-  typedef float float4_t __attribute__((ext_vector_type(4)));
   constexpr int kRows = 16 * T;
   __shared__ float part[SK][kRows][8];
   const int lane = threadIdx.x & (kWave - 1);
@@ -365,9 +363,9 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
     }
   };
 
-  float4_t d[T];
+  mfma_float4_t d[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < T; ++t) d[t] = mfma_float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // unit q + 1's loads are in flight while unit q is decoded; its x is
   // staged after unit q's last MFMA
   uint4 xr[kXLoads], wv[2][T];
@@ -382,18 +380,8 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
 #pragma unroll
   for (int q = 0; q < UPW; ++q) {
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const half8_t b = __builtin_bit_cast(half8_t, xs[s][q & 1][brow + v]);
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const uint32_t wd = (&wv[q & 1][t].x)[v >> 1];
-        const int h = v & 1;
-        const uint4 ap = make_uint4(code_pair(wd, 4 * h + 0), code_pair(wd, 4 * h + 1), code_pair(wd, 4 * h + 2),
-                                    code_pair(wd, 4 * h + 3));
-        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
-      }
-    }
+    mfma_unit_half<0, T>(wv[q & 1], &xs[s][q & 1][brow], d);
+    mfma_unit_half<1, T>(wv[q & 1], &xs[s][q & 1][brow], d);
     if (q + 1 < UPW) {
       stage_x(q + 1, xr);
       if (q + 2 < UPW) {
