@@ -273,13 +273,15 @@ hipError_t launch_swiglu_gate_up_small(const uint32_t* gate, const float* gate_s
                                        int m, uint16_t* h, hipStream_t stream) {
   if (m == 1) return launch_swiglu_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
   // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from
-  // graph-timed sweeps on MI355X at d_ff = 12,288: three tiles (24 pairs, 512
-  // workgroups) of 4 waves up to m = 4 (7.7-8.2 us), six tiles of 8 waves
-  // beyond (8.9 us at m = 8); four tiles took 9.3-10.6 us.
-  if (d_ff >= 8192 && m <= 4) {
+  // graph-timed sweeps on MI355X at d_ff = 12,288 (settled clocks, both
+  // orders): three tiles (24 pairs, 512 workgroups) of 4 waves at m = 2
+  // (7.54 us), six tiles of 8 waves from m = 3 (7.65 / 7.67 / 8.11 us at m =
+  // 3 / 4 / 8, against 7.84-7.87 / 7.87-8.01 / 8.78 for three tiles of 4
+  // waves); four tiles took 9.3-10.6 us in an earlier sweep.
+  if (d_ff >= 8192 && m == 2) {
     launch_gate_up_mfma<4, 3, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   } else if (d_ff >= 8192) {
-    launch_gate_up_mp<8, 6, 2, 8>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+    launch_gate_up_mfma<8, 6, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   } else {
     launch_gate_up_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   }

@@ -568,17 +568,17 @@ hipError_t launch_ternary_gemm_small(const uint32_t* packed, const float* scale,
     // Launch shapes from graph-timed sweeps on MI355X at M = 2..8, clocks
     // settled, each shape timed in both orders. More tiles per workgroup
     // (each activation column reused by more rows) beat more waves down to
-    // about 192-256 workgroups. n = 12,288: 3 tiles, 16 waves at m = 3, 4
-    // (5.37 us; 4 waves 5.57-5.59) and 4 otherwise (5.33 us at m = 2, 5.94 at
-    // m = 8); the q|k|v pack, n = 6,144: 2 tiles (4.45 us at m = 4), one tile
+    // about 192-256 workgroups. n = 12,288 (re-swept with the shared-shift
+    // decode): 3 tiles of 4 waves at m = 2 (5.08 us), of 8 waves from m = 3
+    // (5.11 / 5.21 / 5.67 us at m = 3 / 4 / 8, against 5.26-5.32 / 5.35-5.37 /
+    // 5.73-5.80 for 4 or 16 waves); the q|k|v pack, n = 6,144: 2 tiles (4.45 us at m = 4), one tile
     // of 16 waves at m = 2 (4.25 us); n < 5,120: one tile, 8 waves (q 3.39 /
     // 3.55 / 3.52 / 3.96 us at m = 2 / 3 / 4 / 8; 16 waves 3.48-3.73); K =
     // 8,192: 8 waves (4.69 / 5.50 us at m = 4 / 8); K = 12,288: 8 waves up to
     // m = 4 (5.33 / 6.08 us at m = 2 / 4), 12 beyond (7.36 us at m = 8).
     if (units <= 16) {
       if (n >= 8192 && m == 2) launch_mfma_mp<4, 3, 4, 2>(packed, scale, n, k, x, m, y, stream);
-      else if (n >= 8192 && m <= 4) launch_mfma_mp<16, 3, 1, 4>(packed, scale, n, k, x, m, y, stream);
-      else if (n >= 8192) launch_mfma_mp<4, 3, 4, 8>(packed, scale, n, k, x, m, y, stream);
+      else if (n >= 8192) launch_mfma_cfg<8, 3, 2>(packed, scale, n, k, x, m, y, stream);
       else if (n >= 5120 && m == 2) launch_mfma_mp<16, 1, 1, 2>(packed, scale, n, k, x, m, y, stream);
       else if (n >= 5120 && m <= 4) launch_mfma_mp<4, 2, 4, 4>(packed, scale, n, k, x, m, y, stream);
       else if (n >= 5120) launch_mfma_mp<4, 2, 4, 8>(packed, scale, n, k, x, m, y, stream);
