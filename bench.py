@@ -638,6 +638,12 @@ def main():
         extra["launch_floor_us"] = round(ms * 1e3, 3)
         del g, one
 
+    # each linear at M = 1 against the HBM peak: its fraction, and the time a
+    # launch would take at 75 % of the peak (the per-linear goal)
+    extra["frac_of_peak_per_launch"] = {p: round(v / HBM_PEAK_GBS, 4) for p, v in extra["GBs_per_launch"].items()}
+    extra["us_at_75pct_of_peak"] = {p: round(ternary_bytes(*synth.SHAPES[p]) / (0.75 * HBM_PEAK_GBS * 1e3), 3)
+                                    for p in extra["GBs_per_launch"]}
+
     result = {
         "metric": METRIC,
         "value": round(value, 1),

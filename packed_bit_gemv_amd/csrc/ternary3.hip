@@ -332,13 +332,53 @@ __global__ __launch_bounds__(4 * kWave) void ternary3_generic_kernel(const uint3
   }
 }
 
-// Magnitude bits of pair t of sign/nonzero word `word` (0..3) of a chunk, at
-// bits 10 and 26, from the chunk's magnitude words m0 (words 0, 1) and m1
-// (words 2, 3). Bits 8i + t and 16 + 8i + t of the word's magnitude word (i =
-// word & 1) move there with one 32-bit shift; word and t are compile-time
-// constants wherever this is inlined.
-__device__ __forceinline__ uint32_t mag_of(uint32_t m0, uint32_t m1, int word, int t) {
-  return mag_pair(word < 2 ? m0 : m1, word & 1, t);
+// The four operands of pair T of a chunk (sign/nonzero words lo = w1:w0 and
+// hi = w3:w2, magnitude words m = m1:m0) with their magnitude bits.
+template <int T>
+__device__ __forceinline__ void pair3_ops(uint64_t lo, uint64_t hi, uint64_t m, uint32_t& o0, uint32_t& o1,
+                                          uint32_t& o2, uint32_t& o3) {
+  pair_ops<T>(lo, o0, o1);
+  pair_ops<T>(hi, o2, o3);
+  const uint64_t ma = mag_a<T>(m), mb = mag_b<T>(m);
+  o0 = with_mag(o0, static_cast<uint32_t>(ma));
+  o1 = with_mag(o1, static_cast<uint32_t>(mb));
+  o2 = with_mag(o2, static_cast<uint32_t>(ma >> 32));
+  o3 = with_mag(o3, static_cast<uint32_t>(mb >> 32));
+}
+
+// Matrix-core A operands of half H of a chunk: a[w] holds codes 8H .. 8H + 7
+// of word w as eight fp16 2*c (chunk_half_ops of the 2-bit layout with the
+// magnitude bits OR-ed in; every 64-bit shift serves two words).
+template <int H>
+__device__ __forceinline__ void chunk3_half_ops(const uint4& c, const uint2& mg, uint4 (&a)[4]) {
+  const uint64_t lo = static_cast<uint64_t>(c.y) << 32 | c.x;
+  const uint64_t hi = static_cast<uint64_t>(c.w) << 32 | c.z;
+  const uint64_t m = static_cast<uint64_t>(mg.y) << 32 | mg.x;
+  uint32_t o[4][4];
+  pair3_ops<4 * H + 0>(lo, hi, m, o[0][0], o[1][0], o[2][0], o[3][0]);
+  pair3_ops<4 * H + 1>(lo, hi, m, o[0][1], o[1][1], o[2][1], o[3][1]);
+  pair3_ops<4 * H + 2>(lo, hi, m, o[0][2], o[1][2], o[2][2], o[3][2]);
+  pair3_ops<4 * H + 3>(lo, hi, m, o[0][3], o[1][3], o[2][3], o[3][3]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) a[w] = make_uint4(o[w][0], o[w][1], o[w][2], o[w][3]);
+}
+
+// Half H of one 256-column unit for T tiles (mfma_unit_half of the 2-bit
+// layout): word w's half H against B slot 2w + H, the 4 slots read once.
+template <int H, int T>
+__device__ __forceinline__ void mfma3_unit_half(const uint4 (&wv)[T], const uint2 (&mv)[T], const uint4* xb,
+                                                mfma_float4_t (&d)[T]) {
+  mfma_half8_t b[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) b[w] = __builtin_bit_cast(mfma_half8_t, xb[2 * w + H]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    uint4 a[4];
+    chunk3_half_ops<H>(wv[t], mv[t], a);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mfma_half8_t, a[w]), b[w], d[t], 0, 0, 0);
+  }
 }
 
 // 2 <= M <= 8 on the matrix cores (k % 8 == 0, x 16-byte aligned): the 2-bit
@@ -354,8 +394,6 @@ __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uin
                                                                         int64_t k, int64_t chunks,
                                                                         const uint16_t* __restrict__ x, int m,
                                                                         float* __restrict__ y) {
-  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-  typedef float float4_t __attribute__((ext_vector_type(4)));
   constexpr int kRows = 16 * T;
   __shared__ float part[SK][kRows][8];
   const int lane = threadIdx.x & (kWave - 1);
@@ -406,9 +444,9 @@ __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uin
     }
   };
 
-  float4_t d[T];
+  mfma_float4_t d[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) d[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < T; ++t) d[t] = mfma_float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   uint4 xr[kXLoads], wv[2][T];
   uint2 mv[2][T];
   load_x(0, xr);
@@ -422,21 +460,8 @@ __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uin
 #pragma unroll
   for (int q = 0; q < UPW; ++q) {
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const half8_t b = __builtin_bit_cast(half8_t, xs[s][q & 1][brow + v]);
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int word = v >> 1, h = v & 1;
-        const uint32_t wd = (&wv[q & 1][t].x)[word];
-        const uint32_t m0 = mv[q & 1][t].x, m1 = mv[q & 1][t].y;
-        const uint4 ap = make_uint4(code_pair(wd, 4 * h + 0) | mag_of(m0, m1, word, 4 * h + 0),
-                                    code_pair(wd, 4 * h + 1) | mag_of(m0, m1, word, 4 * h + 1),
-                                    code_pair(wd, 4 * h + 2) | mag_of(m0, m1, word, 4 * h + 2),
-                                    code_pair(wd, 4 * h + 3) | mag_of(m0, m1, word, 4 * h + 3));
-        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ap), b, d[t], 0, 0, 0);
-      }
-    }
+    mfma3_unit_half<0, T>(wv[q & 1], mv[q & 1], &xs[s][q & 1][brow], d);
+    mfma3_unit_half<1, T>(wv[q & 1], mv[q & 1], &xs[s][q & 1][brow], d);
     if (q + 1 < UPW) {
       stage_x(q + 1, xr);
       if (q + 2 < UPW) {

@@ -48,6 +48,12 @@ def test_bench_json_line():
     # the loads alone of the same packed bytes, one launch each
     assert 0 < r["read_ceiling_us"] and 0 < r["frac_of_read_ceiling"] < 1.5
     assert d["extra"]["stream_read_us"]["gate_12.6MB"] > 0
+    # each linear against the HBM peak, and its time at 75 % of it
+    ex = d["extra"]
+    assert set(ex["frac_of_peak_per_launch"]) == set(ex["GBs_per_launch"]) >= {"gate", "up", "down"}
+    for p, f in ex["frac_of_peak_per_launch"].items():
+        assert abs(f - ex["GBs_per_launch"][p] / 8000.0) < 1e-3
+    assert ex["us_at_75pct_of_peak"]["gate"] == 2.115 and ex["us_at_75pct_of_peak"]["down"] == 2.107
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "GB/s" and c["value"] > 0
     assert c["cores"] == len(os.sched_getaffinity(0))  # the CPUs this process may use
