@@ -27,7 +27,8 @@ What it computes (Neutrino-1 8B model page, English text on bittide):
 * The feed-forward block is gated (SwiGLU) with three linears per layer
   (geometry table): h = silu(gate x) * (up x), rounded to fp16, then down h.
   The page names the gate but not its formula; silu(z) = z * sigmoid(z) is
-  the usual reading.
+  the usual reading. The same block is also computed with the three linears
+  in the 3-bit layout below (ffn3_swiglu).
 
 Bit layout of one 32-bit word (little-endian uint32) holding 16 codes:
   code j (0..15) belongs to pair t = j // 2 and half h = j % 2;
@@ -71,7 +72,10 @@ Parity pins: see tests/test_oracle.py (exhaustive single-word round trip,
 hand-written format words, the fp16 reading of the layout, brute force
 over all ternary rows for K <= 8 against exact rational sums, closed forms,
 exact integer matmul for the head, the row-sum and count invariants, silu at
-closed-form points and its Lambert-W minimum, an integer SwiGLU probe).
+closed-form points and its Lambert-W minimum, an integer SwiGLU probe; for
+the 3-bit feed-forward block, its equality with the 2-bit block on ternary
+codes, the doubled-codes / doubled-scales identity and a five-level integer
+probe).
 """
 from __future__ import annotations
 
@@ -406,3 +410,21 @@ def ternary3_gemv(packed: np.ndarray, scale: np.ndarray, k: int, x: np.ndarray) 
     if x.ndim != 1:
         raise ValueError("ternary3_gemv takes one activation row")
     return ternary3_gemm_small(packed, scale, k, x[None, :])[0]
+
+
+def ffn3_swiglu(gate_packed: np.ndarray, gate_scale: np.ndarray, up_packed: np.ndarray, up_scale: np.ndarray,
+                down_packed: np.ndarray, down_scale: np.ndarray, d_model: int, x: np.ndarray):
+    """ffn_swiglu with the three linears in the 3-bit layout: g = gate x,
+    u = up x, h = fp16(silu(g) * u), y = down h, each linear five-level with
+    per-row scales (Neutrino-1 8B model page: geometry table for the block,
+    "Where the bytes live" for the 3-bit coded lane). Returns (h fp16 [m, d_ff],
+    y fp64 [m, d_model]).
+    """
+    d_ff = gate_packed.shape[0]
+    if up_packed.shape[0] != d_ff or down_packed.shape[0] != d_model:
+        raise ValueError("gate and up are [d_ff, .], down is [d_model, .]")
+    g = ternary3_gemm_small(gate_packed, gate_scale, d_model, x)
+    u = ternary3_gemm_small(up_packed, up_scale, d_model, x)
+    h = (silu(g) * u).astype(np.float16)
+    y = ternary3_gemm_small(down_packed, down_scale, d_ff, h)
+    return h, y

@@ -640,3 +640,63 @@ def test_row_sums_and_counts3():
     assert counts.sum() == codes.size
     hist = np.bincount((codes.astype(np.int64) + 2).ravel(), minlength=5)
     assert counts.tolist() == hist.tolist()
+
+
+# --------------------------------------------------------------------------
+# The feed-forward block in the 3-bit layout
+# --------------------------------------------------------------------------
+def test_ffn3_on_ternary_codes_is_the_2bit_block():
+    """Codes in {-1, 0, +1} packed in the 3-bit layout give the 2-bit block's h and y bit for bit."""
+    d_model, d_ff = 192, 136
+    x = synth.activations(60, 2, d_model)
+    g, u = synth.ternary_codes(61, d_ff, d_model), synth.ternary_codes(62, d_ff, d_model)
+    d = synth.ternary_codes(63, d_model, d_ff)
+    sg, su, sd = synth.row_scales(64, d_ff), synth.row_scales(65, d_ff), synth.row_scales(66, d_model)
+    h2, y2 = oracle.ffn_swiglu(oracle.pack(g)[0], sg, oracle.pack(u)[0], su, oracle.pack(d)[0], sd, d_model, x)
+    h3, y3 = oracle.ffn3_swiglu(oracle.pack3(g)[0], sg, oracle.pack3(u)[0], su, oracle.pack3(d)[0], sd, d_model, x)
+    assert np.array_equal(h2, h3) and np.array_equal(y2, y3)
+
+
+def test_ffn3_doubled_codes_equal_doubled_scales():
+    """Codes 2c in the 3-bit layout with scale s equal codes c with scale 2s (exact in fp32), in each of the
+    three linears at once: a dropped or misplaced magnitude anywhere in the block breaks the equality."""
+    d_model, d_ff = 256, 200
+    x = synth.activations(67, 3, d_model)
+    g, u = synth.ternary_codes(68, d_ff, d_model), synth.ternary_codes(69, d_ff, d_model)
+    d = synth.ternary_codes(70, d_model, d_ff)
+    sg, su, sd = synth.row_scales(71, d_ff), synth.row_scales(72, d_ff), synth.row_scales(73, d_model)
+    h2, y2 = oracle.ffn_swiglu(oracle.pack(g)[0], 2 * sg, oracle.pack(u)[0], su, oracle.pack(d)[0], 2 * sd,
+                               d_model, x)
+    h3, y3 = oracle.ffn3_swiglu(oracle.pack3(2 * g)[0], sg, oracle.pack3(u)[0], su, oracle.pack3(2 * d)[0], sd,
+                                d_model, x)
+    assert np.array_equal(h2, h3) and np.array_equal(y2, y3)
+    # and the doubled up linear doubles h: silu(g) * 2u rounds to fp16 as twice the rounding of silu(g) * u
+    # wherever both are normal fp16 numbers (below 2^-14 the rounding step no longer scales with the value)
+    h4, _ = oracle.ffn3_swiglu(oracle.pack3(g)[0], sg, oracle.pack3(2 * u)[0], su, oracle.pack3(d)[0], sd, d_model, x)
+    h1, _ = oracle.ffn3_swiglu(oracle.pack3(g)[0], sg, oracle.pack3(u)[0], su, oracle.pack3(d)[0], sd, d_model, x)
+    normal = np.abs(h1.astype(np.float64)) >= 2.0 ** -14
+    assert normal.mean() > 0.9
+    assert np.array_equal(h4.astype(np.float64)[normal], 2 * h1.astype(np.float64)[normal])
+
+
+def test_ffn3_integer_probe_exact():
+    """Five-level probe: the 2-bit probe with the gate codes of rows r = 0 mod 3 and the up codes of rows
+    r = 1 mod 4 doubled, so g = +-2|S_r| or +-|S_r| (|g| >= 40) and u is an integer; h = g * u (rounded
+    once to fp16) or 0, and y = s_d * (C_down @ h) with five-level down codes, all in exact integers."""
+    d_model, d_ff = 192, 136
+    x, gate, up, _, h2 = _ffn_probe(74, d_model, d_ff)
+    r = np.arange(d_ff)
+    gmul = np.where(r % 3 == 0, 2, 1)
+    umul = np.where(r % 4 == 1, 2, 1)
+    gate3 = (gate.astype(np.int16) * gmul[:, None]).astype(np.int8)
+    up3 = (up.astype(np.int16) * umul[:, None]).astype(np.int8)
+    down3 = synth.ternary3_codes(75, d_model, d_ff)
+    h_exp = (h2 * gmul * umul).astype(np.float16).astype(np.float64)
+    one_f = np.ones(d_ff, dtype=np.float32)
+    s_d = synth.pow2_scales(76, d_model)
+    h, y = oracle.ffn3_swiglu(oracle.pack3(gate3)[0], one_f, oracle.pack3(up3)[0], one_f, oracle.pack3(down3)[0], s_d,
+                              d_model, x)
+    assert np.array_equal(h[0].astype(np.float64), h_exp)
+    assert np.count_nonzero(np.abs(down3) == 2) > 0 and np.count_nonzero(h_exp) > d_ff // 2
+    y_exp = (down3.astype(np.int64) @ h_exp.astype(np.int64)).astype(np.float64) * s_d.astype(np.float64)
+    assert np.array_equal(y[0], y_exp)
