@@ -354,6 +354,41 @@ int ternary_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scal
                              hipStream_t stream);
 
 /*
+ * ternary3_swiglu_gate_up, ternary3_ffn_swiglu, ternary3_swiglu_gate_up_small,
+ * ternary3_ffn_swiglu_small - the four SwiGLU feed-forward calls above with
+ * the three linears in the 3-bit layout (five-level codes, see
+ * ternary3_gemv): the same h = fp16(silu(gate x) * up x) and y = down h, one
+ * launch for gate and up together, then ternary3_gemv (m = 1) or
+ * ternary3_gemm_small (m rows) of down on h.
+ * Source: Neutrino-1 8B model page, geometry table (gated SwiGLU block, three
+ * linears) and "Where the bytes live" (the coded lane at 3 bits per weight,
+ * per-row scales).
+ *
+ *   gate_packed, up_packed  [d_ff][pbg_words_per_row3(d_model)] uint32,
+ *                           16-byte aligned
+ *   down_packed             [d_model][pbg_words_per_row3(d_ff)] uint32,
+ *                           16-byte aligned
+ * Everything else (scales, x, h, y, m, limits, alignment, return codes) is as
+ * for the 2-bit calls of the same name without the 3.
+ */
+int ternary3_swiglu_gate_up(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                            const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
+                            hipStream_t stream);
+
+int ternary3_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                        const float* up_scale, const uint32_t* down_packed, const float* down_scale, int64_t d_model,
+                        int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream);
+
+int ternary3_swiglu_gate_up_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                                  const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m,
+                                  uint16_t* h, hipStream_t stream);
+
+int ternary3_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                              const float* up_scale, const uint32_t* down_packed, const float* down_scale,
+                              int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m, uint16_t* h, float* y,
+                              hipStream_t stream);
+
+/*
  * pbg_stream_read - measurement helper, not a step of the decode path: reads
  * `bytes` of device memory once with the loads the GEMV kernels use (16-byte
  * non-temporal loads, 1 KiB of consecutive bytes per wave-wide load, up to

@@ -20,8 +20,10 @@ from .binding import (  # noqa: F401
     ternary_gemm_small,
     ternary_gemm_splitk,
     ternary_gemv,
+    ternary3_ffn_swiglu,
     ternary3_gemm_small,
     ternary3_gemv,
+    ternary3_swiglu_gate_up,
     words_per_row,
     words_per_row3,
 )
@@ -42,8 +44,10 @@ __all__ = [
     "ternary_gemm_small",
     "ternary_gemm_splitk",
     "ternary_gemv",
+    "ternary3_ffn_swiglu",
     "ternary3_gemm_small",
     "ternary3_gemv",
+    "ternary3_swiglu_gate_up",
     "words_per_row",
     "words_per_row3",
 ]

@@ -47,6 +47,11 @@ _SIGNATURES = {
     "ternary_swiglu_gate_up_small": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "ternary_ffn_swiglu_small": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp,
                                           _vp]),
+    "ternary3_ffn_swiglu_small": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp,
+                                           _vp]),
+    "ternary3_swiglu_gate_up": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "ternary3_ffn_swiglu": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "ternary3_swiglu_gate_up_small": (_c_int, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]),
     "pbg_stream_read": (_c_int, [_vp, _c_i64, _vp, _vp]),
 }
 
@@ -407,20 +412,15 @@ def _ffn_rows(x: torch.Tensor, d_model: int) -> int:
     raise ValueError(f"x must be [{d_model}] or [m, {d_model}] with 1 <= m <= {MAX_M}")
 
 
-def ternary_swiglu_gate_up(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
-                           d_model: int, x: torch.Tensor, h: torch.Tensor | None = None) -> torch.Tensor:
-    """h = fp16(silu(gate x) * up x) in one launch; gate, up packed [d_ff, words_per_row(d_model)].
-
-    x fp16 [d_model] gives h [d_ff]; x [m, d_model] (m <= 8, one weight read for all rows) gives h [m, d_ff].
-    """
+def _swiglu_gate_up(prefix: str, wpr, gate, gate_scale, up, up_scale, d_model, x, h):
     for t, name in ((gate, "gate"), (up, "up")):
         _dev(t, name, torch.int32)
     for t, name in ((gate_scale, "gate_scale"), (up_scale, "up_scale")):
         _dev(t, name, torch.float32)
     _dev(x, "x", torch.float16)
     d_ff = gate.shape[0]
-    if gate.dim() != 2 or tuple(up.shape) != tuple(gate.shape) or gate.shape[1] != words_per_row(d_model):
-        raise ValueError(f"gate and up must be [d_ff, {words_per_row(d_model)}]")
+    if gate.dim() != 2 or tuple(up.shape) != tuple(gate.shape) or gate.shape[1] != wpr(d_model):
+        raise ValueError(f"gate and up must be [d_ff, {wpr(d_model)}]")
     if tuple(gate_scale.shape) != (d_ff,) or tuple(up_scale.shape) != (d_ff,):
         raise ValueError("scales must be [d_ff]")
     m = _ffn_rows(x, d_model)
@@ -431,36 +431,43 @@ def ternary_swiglu_gate_up(gate: torch.Tensor, gate_scale: torch.Tensor, up: tor
     if tuple(h.shape) != h_shape:
         raise ValueError(f"h must be {list(h_shape)}")
     if m == 0:
-        rc = lib().ternary_swiglu_gate_up(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
-                                          d_model, d_ff, x.data_ptr(), h.data_ptr(), _stream(gate))
-        _check("ternary_swiglu_gate_up", rc)
+        name = f"{prefix}_swiglu_gate_up"
+        rc = getattr(lib(), name)(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                  d_model, d_ff, x.data_ptr(), h.data_ptr(), _stream(gate))
     else:
-        rc = lib().ternary_swiglu_gate_up_small(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(),
-                                                up_scale.data_ptr(), d_model, d_ff, x.data_ptr(), m, h.data_ptr(),
-                                                _stream(gate))
-        _check("ternary_swiglu_gate_up_small", rc)
+        name = f"{prefix}_swiglu_gate_up_small"
+        rc = getattr(lib(), name)(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                  d_model, d_ff, x.data_ptr(), m, h.data_ptr(), _stream(gate))
+    _check(name, rc)
     return h
 
 
-def ternary_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
-                       down: torch.Tensor, down_scale: torch.Tensor, x: torch.Tensor,
-                       h: torch.Tensor | None = None, y: torch.Tensor | None = None):
-    """Gated feed-forward block: h = fp16(silu(gate x) * up x), y = down h.
+def ternary_swiglu_gate_up(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
+                           d_model: int, x: torch.Tensor, h: torch.Tensor | None = None) -> torch.Tensor:
+    """h = fp16(silu(gate x) * up x) in one launch; gate, up packed [d_ff, words_per_row(d_model)].
 
-    gate, up: packed [d_ff, words_per_row(d_model)]; down: packed [d_model, words_per_row(d_ff)];
-    x fp16 [d_model] -> (h fp16 [d_ff], y fp32 [d_model]), or x [m, d_model] with m <= 8 ->
-    (h [m, d_ff], y [m, d_model]), each weight read once for all m rows.
+    x fp16 [d_model] gives h [d_ff]; x [m, d_model] (m <= 8, one weight read for all rows) gives h [m, d_ff].
     """
+    return _swiglu_gate_up("ternary", words_per_row, gate, gate_scale, up, up_scale, d_model, x, h)
+
+
+def ternary3_swiglu_gate_up(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
+                            d_model: int, x: torch.Tensor, h: torch.Tensor | None = None) -> torch.Tensor:
+    """ternary_swiglu_gate_up with gate and up in the 3-bit layout, packed [d_ff, words_per_row3(d_model)]."""
+    return _swiglu_gate_up("ternary3", words_per_row3, gate, gate_scale, up, up_scale, d_model, x, h)
+
+
+def _ffn_swiglu(prefix: str, wpr, gate, gate_scale, up, up_scale, down, down_scale, x, h, y):
     for t, name in ((gate, "gate"), (up, "up"), (down, "down")):
         _dev(t, name, torch.int32)
     for t, name in ((gate_scale, "gate_scale"), (up_scale, "up_scale"), (down_scale, "down_scale")):
         _dev(t, name, torch.float32)
     _dev(x, "x", torch.float16)
     d_ff, d_model = gate.shape[0], down.shape[0]
-    if gate.dim() != 2 or tuple(up.shape) != tuple(gate.shape) or gate.shape[1] != words_per_row(d_model):
-        raise ValueError(f"gate and up must be [d_ff, {words_per_row(d_model)}]")
-    if down.dim() != 2 or down.shape[1] != words_per_row(d_ff):
-        raise ValueError(f"down must be [d_model, {words_per_row(d_ff)}]")
+    if gate.dim() != 2 or tuple(up.shape) != tuple(gate.shape) or gate.shape[1] != wpr(d_model):
+        raise ValueError(f"gate and up must be [d_ff, {wpr(d_model)}]")
+    if down.dim() != 2 or down.shape[1] != wpr(d_ff):
+        raise ValueError(f"down must be [d_model, {wpr(d_ff)}]")
     if tuple(gate_scale.shape) != (d_ff,) or tuple(up_scale.shape) != (d_ff,) or tuple(down_scale.shape) != (d_model,):
         raise ValueError("scales must be [d_ff], [d_ff], [d_model]")
     m = _ffn_rows(x, d_model)
@@ -476,16 +483,36 @@ def ternary_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.T
     if tuple(h.shape) != h_shape or tuple(y.shape) != y_shape:
         raise ValueError(f"h must be {list(h_shape)} and y {list(y_shape)}")
     if m == 0:
-        rc = lib().ternary_ffn_swiglu(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
-                                      down.data_ptr(), down_scale.data_ptr(), d_model, d_ff, x.data_ptr(),
-                                      h.data_ptr(), y.data_ptr(), _stream(gate))
-        _check("ternary_ffn_swiglu", rc)
+        name = f"{prefix}_ffn_swiglu"
+        rc = getattr(lib(), name)(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                  down.data_ptr(), down_scale.data_ptr(), d_model, d_ff, x.data_ptr(), h.data_ptr(),
+                                  y.data_ptr(), _stream(gate))
     else:
-        rc = lib().ternary_ffn_swiglu_small(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(),
-                                            up_scale.data_ptr(), down.data_ptr(), down_scale.data_ptr(), d_model,
-                                            d_ff, x.data_ptr(), m, h.data_ptr(), y.data_ptr(), _stream(gate))
-        _check("ternary_ffn_swiglu_small", rc)
+        name = f"{prefix}_ffn_swiglu_small"
+        rc = getattr(lib(), name)(gate.data_ptr(), gate_scale.data_ptr(), up.data_ptr(), up_scale.data_ptr(),
+                                  down.data_ptr(), down_scale.data_ptr(), d_model, d_ff, x.data_ptr(), m,
+                                  h.data_ptr(), y.data_ptr(), _stream(gate))
+    _check(name, rc)
     return h, y
+
+
+def ternary_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
+                       down: torch.Tensor, down_scale: torch.Tensor, x: torch.Tensor,
+                       h: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """Gated feed-forward block: h = fp16(silu(gate x) * up x), y = down h.
+
+    gate, up: packed [d_ff, words_per_row(d_model)]; down: packed [d_model, words_per_row(d_ff)];
+    x fp16 [d_model] -> (h fp16 [d_ff], y fp32 [d_model]), or x [m, d_model] with m <= 8 ->
+    (h [m, d_ff], y [m, d_model]), each weight read once for all m rows.
+    """
+    return _ffn_swiglu("ternary", words_per_row, gate, gate_scale, up, up_scale, down, down_scale, x, h, y)
+
+
+def ternary3_ffn_swiglu(gate: torch.Tensor, gate_scale: torch.Tensor, up: torch.Tensor, up_scale: torch.Tensor,
+                        down: torch.Tensor, down_scale: torch.Tensor, x: torch.Tensor,
+                        h: torch.Tensor | None = None, y: torch.Tensor | None = None):
+    """ternary_ffn_swiglu with the three linears in the 3-bit layout (rows of words_per_row3 words)."""
+    return _ffn_swiglu("ternary3", words_per_row3, gate, gate_scale, up, up_scale, down, down_scale, x, h, y)
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:

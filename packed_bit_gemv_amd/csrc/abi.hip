@@ -244,4 +244,60 @@ int ternary_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scal
                                              d_model, d_ff, x, static_cast<int>(m), h, y, stream));
 }
 
+int ternary3_swiglu_gate_up(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                            const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
+                            hipStream_t stream) {
+  if (!gate_packed || !gate_scale || !up_packed || !up_scale || !x || !h) return PBG_ERR_NULL;
+  if (bad_ffn(d_model, d_ff)) return PBG_ERR_SHAPE;
+  if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(gate_scale, 4) ||
+      misaligned(up_scale, 4) || misaligned(x, 16) || misaligned(h, 16))
+    return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_swiglu3_gate_up(gate_packed, gate_scale, up_packed, up_scale, d_model, d_ff, x, h, stream));
+}
+
+int ternary3_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                        const float* up_scale, const uint32_t* down_packed, const float* down_scale, int64_t d_model,
+                        int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream) {
+  if (!gate_packed || !gate_scale || !up_packed || !up_scale || !down_packed || !down_scale || !x || !h || !y)
+    return PBG_ERR_NULL;
+  if (bad_ffn(d_model, d_ff)) return PBG_ERR_SHAPE;
+  if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(down_packed, 16) ||
+      misaligned(gate_scale, 4) || misaligned(up_scale, 4) || misaligned(down_scale, 4) || misaligned(x, 16) ||
+      misaligned(h, 16) || misaligned(y, 4))
+    return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_ffn3_swiglu(gate_packed, gate_scale, up_packed, up_scale, down_packed, down_scale, d_model,
+                                        d_ff, x, h, y, stream));
+}
+
+int ternary3_swiglu_gate_up_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                                  const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m,
+                                  uint16_t* h, hipStream_t stream) {
+  if (!gate_packed || !gate_scale || !up_packed || !up_scale || !x || !h) return PBG_ERR_NULL;
+  if (bad_ffn(d_model, d_ff) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(gate_scale, 4) ||
+      misaligned(up_scale, 4) || misaligned(x, 16) || misaligned(h, 16))
+    return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_swiglu3_gate_up_small(gate_packed, gate_scale, up_packed, up_scale, d_model, d_ff, x,
+                                                  static_cast<int>(m), h, stream));
+}
+
+int ternary3_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
+                              const float* up_scale, const uint32_t* down_packed, const float* down_scale,
+                              int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m, uint16_t* h, float* y,
+                              hipStream_t stream) {
+  if (!gate_packed || !gate_scale || !up_packed || !up_scale || !down_packed || !down_scale || !x || !h || !y)
+    return PBG_ERR_NULL;
+  if (bad_ffn(d_model, d_ff) || bad_m(m)) return PBG_ERR_SHAPE;
+  if (misaligned(gate_packed, 16) || misaligned(up_packed, 16) || misaligned(down_packed, 16) ||
+      misaligned(gate_scale, 4) || misaligned(up_scale, 4) || misaligned(down_scale, 4) || misaligned(x, 16) ||
+      misaligned(h, 16) || misaligned(y, 4))
+    return PBG_ERR_ALIGN;
+  if (pending_error()) return PBG_ERR_HIP;
+  return finish(pbg::launch_ffn3_swiglu_small(gate_packed, gate_scale, up_packed, up_scale, down_packed, down_scale,
+                                              d_model, d_ff, x, static_cast<int>(m), h, y, stream));
+}
+
 }  // extern "C"

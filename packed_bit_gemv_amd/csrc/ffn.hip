@@ -29,10 +29,6 @@ namespace {
 constexpr int kPairs = 2;      // row pairs per wave
 constexpr int kFfnWaves = 4;   // waves per workgroup
 
-// z * sigmoid(z) with the hardware reciprocal (1 ulp): h is rounded to fp16
-// right after, so an IEEE division would only cost instructions.
-__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
-
 template <int R, int G>
 __global__ __launch_bounds__(G* kWave) void swiglu_gate_up_kernel(
     const uint4* __restrict__ gate, const float* __restrict__ gate_scale, const uint4* __restrict__ up,

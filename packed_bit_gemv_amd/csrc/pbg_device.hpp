@@ -122,6 +122,11 @@ __device__ __forceinline__ void chunk_half_ops(const uint4& c, uint4 (&a)[4]) {
   for (int w = 0; w < 4; ++w) a[w] = make_uint4(o[w][0], o[w][1], o[w][2], o[w][3]);
 }
 
+// z * sigmoid(z) with the hardware reciprocal (1 ulp), for the SwiGLU
+// epilogues: h is rounded to fp16 right after, so an IEEE division would only
+// cost instructions.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 typedef _Float16 mfma_half8_t __attribute__((ext_vector_type(8)));
 typedef float mfma_float4_t __attribute__((ext_vector_type(4)));
 

@@ -75,4 +75,19 @@ hipError_t launch_ternary3_gemv(const uint32_t* packed, const float* scale, int6
 hipError_t launch_ternary3_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
                                       const uint16_t* x, int m, float* y, hipStream_t stream);
 
+// The SwiGLU block with 3-bit linears (d_model <= PBG_FFN_MAX_MODEL, 16-byte aligned x and h).
+hipError_t launch_swiglu3_gate_up(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                  const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,
+                                  hipStream_t stream);
+hipError_t launch_ffn3_swiglu(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                              const float* up_scale, const uint32_t* down, const float* down_scale, int64_t d_model,
+                              int64_t d_ff, const uint16_t* x, uint16_t* h, float* y, hipStream_t stream);
+hipError_t launch_swiglu3_gate_up_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                        const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x,
+                                        int m, uint16_t* h, hipStream_t stream);
+hipError_t launch_ffn3_swiglu_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
+                                    const float* up_scale, const uint32_t* down, const float* down_scale,
+                                    int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* y,
+                                    hipStream_t stream);
+
 }  // namespace pbg

@@ -83,6 +83,15 @@ int main(void) {
   expect("ffn small null y",
          ternary_ffn_swiglu_small(packed, scale, packed, scale, packed, scale, 4096, 64, x, 4, h, NULL, 0),
          PBG_ERR_NULL);
+  expect("3-bit gate_up d_model not multiple of 8",
+         ternary3_swiglu_gate_up(packed, scale, packed, scale, 100, 64, x, h, 0), PBG_ERR_SHAPE);
+  expect("3-bit ffn d_model too large",
+         ternary3_ffn_swiglu(packed, scale, packed, scale, packed, scale, PBG_FFN_MAX_MODEL + 8, 64, x, h, y, 0),
+         PBG_ERR_SHAPE);
+  expect("3-bit gate_up small m = 0",
+         ternary3_swiglu_gate_up_small(packed, scale, packed, scale, 4096, 64, x, 0, h, 0), PBG_ERR_SHAPE);
+  expect("3-bit ffn small null down",
+         ternary3_ffn_swiglu_small(packed, scale, packed, scale, NULL, scale, 4096, 64, x, 4, h, y, 0), PBG_ERR_NULL);
   expect("stream read bytes not a multiple of 16", pbg_stream_read(w, 1000, (uint32_t*)(base + 0x8000), 0),
          PBG_ERR_SHAPE);
   expect("stream read src misaligned", pbg_stream_read(w + 8, 1024, (uint32_t*)(base + 0x8000), 0), PBG_ERR_ALIGN);

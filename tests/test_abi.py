@@ -123,37 +123,41 @@ def test_strerror_is_static():
 
 
 @no_gpu_only
-def test_ffn_validation():
+@pytest.mark.parametrize("prefix", ["ternary", "ternary3"])
+def test_ffn_validation(prefix):
     lib = binding.lib()
+    ffn, gate_up = getattr(lib, f"{prefix}_ffn_swiglu"), getattr(lib, f"{prefix}_swiglu_gate_up")
     p6 = [GOOD] * 6
-    assert lib.ternary_ffn_swiglu(None, *p6[1:], 4096, 12288, GOOD, GOOD, GOOD, None) == -1
-    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD, GOOD, None, None) == -1
+    assert ffn(None, *p6[1:], 4096, 12288, GOOD, GOOD, GOOD, None) == -1
+    assert ffn(*p6, 4096, 12288, GOOD, GOOD, None, None) == -1
     for dm, dff in ((0, 12288), (4096 + 8, 12288), (100, 12288), (4, 12288), (4096, 0), (4096, 2 ** 24 + 1)):
-        assert lib.ternary_ffn_swiglu(*p6, dm, dff, GOOD, GOOD, GOOD, None) == -2
-    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD + 8, GOOD, GOOD, None) == -3   # x
-    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD, GOOD + 2, GOOD, None) == -3   # h
-    assert lib.ternary_ffn_swiglu(*p6, 4096, 12288, GOOD, GOOD, GOOD + 2, None) == -3   # y
-    assert lib.ternary_ffn_swiglu(GOOD + 4, *p6[1:], 4096, 12288, GOOD, GOOD, GOOD, None) == -3
-    assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, None, None) == -1
-    assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4100, 12288, GOOD, GOOD, None) == -2
-    assert lib.ternary_swiglu_gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, GOOD + 2, None) == -3
+        assert ffn(*p6, dm, dff, GOOD, GOOD, GOOD, None) == -2
+    assert ffn(*p6, 4096, 12288, GOOD + 8, GOOD, GOOD, None) == -3   # x
+    assert ffn(*p6, 4096, 12288, GOOD, GOOD + 2, GOOD, None) == -3   # h
+    assert ffn(*p6, 4096, 12288, GOOD, GOOD, GOOD + 2, None) == -3   # y
+    assert ffn(GOOD + 4, *p6[1:], 4096, 12288, GOOD, GOOD, GOOD, None) == -3
+    assert gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, None, None) == -1
+    assert gate_up(GOOD, GOOD, GOOD, GOOD, 4100, 12288, GOOD, GOOD, None) == -2
+    assert gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, GOOD + 2, None) == -3
 
 
-def test_ffn_small_validation():
+@pytest.mark.parametrize("prefix", ["ternary", "ternary3"])
+def test_ffn_small_validation(prefix):
     lib = binding.lib()
+    ffn, gate_up = getattr(lib, f"{prefix}_ffn_swiglu_small"), getattr(lib, f"{prefix}_swiglu_gate_up_small")
     p6 = [GOOD] * 6
-    assert lib.ternary_ffn_swiglu_small(None, *p6[1:], 4096, 12288, GOOD, 4, GOOD, GOOD, None) == -1
-    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, 4, GOOD, None, None) == -1
+    assert ffn(None, *p6[1:], 4096, 12288, GOOD, 4, GOOD, GOOD, None) == -1
+    assert ffn(*p6, 4096, 12288, GOOD, 4, GOOD, None, None) == -1
     for m in (0, 9, -1):
-        assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, m, GOOD, GOOD, None) == -2
-        assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, m, GOOD, None) == -2
+        assert ffn(*p6, 4096, 12288, GOOD, m, GOOD, GOOD, None) == -2
+        assert gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, m, GOOD, None) == -2
     for dm, dff in ((0, 12288), (4096 + 8, 12288), (100, 12288), (4096, 0)):
-        assert lib.ternary_ffn_swiglu_small(*p6, dm, dff, GOOD, 4, GOOD, GOOD, None) == -2
-    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD + 8, 4, GOOD, GOOD, None) == -3   # x
-    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, 4, GOOD + 2, GOOD, None) == -3   # h
-    assert lib.ternary_ffn_swiglu_small(*p6, 4096, 12288, GOOD, 4, GOOD, GOOD + 2, None) == -3   # y
-    assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, 4, None, None) == -1
-    assert lib.ternary_swiglu_gate_up_small(GOOD, GOOD, GOOD + 4, GOOD, 4096, 12288, GOOD, 4, GOOD, None) == -3
+        assert ffn(*p6, dm, dff, GOOD, 4, GOOD, GOOD, None) == -2
+    assert ffn(*p6, 4096, 12288, GOOD + 8, 4, GOOD, GOOD, None) == -3   # x
+    assert ffn(*p6, 4096, 12288, GOOD, 4, GOOD + 2, GOOD, None) == -3   # h
+    assert ffn(*p6, 4096, 12288, GOOD, 4, GOOD, GOOD + 2, None) == -3   # y
+    assert gate_up(GOOD, GOOD, GOOD, GOOD, 4096, 12288, GOOD, 4, None, None) == -1
+    assert gate_up(GOOD, GOOD, GOOD + 4, GOOD, 4096, 12288, GOOD, 4, GOOD, None) == -3
 
 
 def test_stream_read_validation():
