@@ -67,6 +67,14 @@ def ternary3_bytes(n: int, k: int, m: int = 1) -> int:
     return synth.words3_bytes(n, k) + 4 * n + 2 * m * k + 4 * m * n
 
 
+def ffn3_block_bytes(d_model: int, d_ff: int, m: int = 1) -> int:
+    """Algorithmic bytes of the 3-bit block as it runs: the gate|up launch (both
+    3-bit matrices and scales, x in, h out) plus the down launch on h. At
+    d_model 4,096, d_ff 12,288, m = 1: 37,879,808 + 18,931,712 = 56,811,520."""
+    gate_up = 2 * synth.words3_bytes(d_ff, d_model) + 2 * 4 * d_ff + 2 * m * d_model + 2 * m * d_ff
+    return gate_up + ternary3_bytes(d_model, d_ff, m)
+
+
 def head_bytes(n: int, k: int, m: int = 1) -> int:
     return n * k + 4 * n + 2 * m * k + 4 * m * n
 
@@ -569,17 +577,24 @@ def main():
         # the 3-bit lane (five-level codes, the shipped lane's 72,351,744 bytes
         # of weights per layer): a pool of L layers of the 7 linears, per-linear
         # launches, the read of their packed bytes, and whole layers at M = 1 and 8
-        pool3 = []
+        pool3, fused3 = [], []
         st6 = torch.empty(6, dtype=torch.int64, device=device)
         for l in range(L):
-            lay = {}
+            lay, qkv = {}, []
             for p in synth.PROJECTIONS:
                 n, k = synth.SHAPES[p]
                 seed = synth.tensor_seed(l, p)
                 codes = synth.ternary3_codes_device(seed, n, k, synth.code_dist(l, p), device)
                 lay[p] = (pbg.pack_ternary3(codes, stats=st6, check=False)[0], synth.row_scales_device(seed, n, device),
                           n, k)
+                if p in ("q", "k", "v"):
+                    qkv.append(codes)
                 del codes
+            # q|k|v as one 6,144-row pack (one launch for the three linears of the same x)
+            cat = torch.cat(qkv)
+            fused3.append((pbg.pack_ternary3(cat, stats=st6, check=False)[0],
+                           torch.cat([lay[p][1] for p in ("q", "k", "v")])))
+            del qkv, cat
             pool3.append(lay)
         torch.cuda.synchronize()
 
@@ -617,8 +632,42 @@ def main():
             lane3[f"layer_m{m}_us_36_per_graph"] = round(ms * 1e3, 3)
             lane3[f"layer_m{m}_GBs_36_per_graph"] = round(lb / (ms * 1e-3) / 1e9, 1)
             del g
+        # the SwiGLU block with 3-bit linears (gate|up + SwiGLU in one launch, then
+        # down on h), and the fused layer: q|k|v pack, o, the block (4 launches)
+        h3 = torch.empty((8, synth.FFN), dtype=torch.float16, device=device)
+        y3 = torch.empty((8, synth.HIDDEN), dtype=torch.float32, device=device)
+        yqkv3 = torch.empty((8, fused3[0][0].shape[0]), dtype=torch.float32, device=device)
+
+        def ffn3_block(l, m=1):
+            lay = pool3[l]
+            xin = xs[synth.HIDDEN][0] if m == 1 else xs[synth.HIDDEN][:m]
+            pbg.ternary3_ffn_swiglu(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], lay["down"][0],
+                                    lay["down"][1], xin, h3[0] if m == 1 else h3[:m], y3[0] if m == 1 else y3[:m])
+
+        def fused_layer3(l, m=1):
+            qp, qs = fused3[l]
+            if m == 1:
+                pbg.ternary3_gemv(qp, qs, synth.HIDDEN, xs[synth.HIDDEN][0], yqkv3[0])
+            else:
+                pbg.ternary3_gemm_small(qp, qs, synth.HIDDEN, xs[synth.HIDDEN][:m], yqkv3[:m])
+            linear3(l, "o", m)
+            ffn3_block(l, m)
+
+        for m in (1, 8):
+            g = capture(torch, lambda m=m: [ffn3_block(l, m) for l in range(L)])
+            us = time_graphs(torch, [g], 5, 1) * 1e3 / L
+            fb = ffn3_block_bytes(synth.HIDDEN, synth.FFN, m)
+            lane3[f"ffn_block_m{m}_us"] = round(us, 3)
+            lane3[f"ffn_block_m{m}_GBs"] = round(fb / (us * 1e-6) / 1e9, 1)
+            del g
+            lb = sum(ternary3_bytes(*synth.SHAPES[p], m) for p in synth.PROJECTIONS)
+            g = capture(torch, lambda m=m: [fused_layer3(l, m) for l in range(L)])
+            ms = time_graphs(torch, [g], 5, 1) / L
+            lane3[f"layer_fused_m{m}_us_36_per_graph"] = round(ms * 1e3, 3)
+            lane3[f"layer_fused_m{m}_GBs_36_per_graph"] = round(lb / (ms * 1e-3) / 1e9, 1)
+            del g
         extra["lane3"] = lane3
-        del pool3
+        del pool3, fused3, h3, y3, yqkv3
 
         # streaming-read ceiling at the gate byte count: torch copy over a pool
         nbytes = synth.words_bytes(*synth.SHAPES["gate"])

@@ -18,6 +18,9 @@
 namespace pbg {
 namespace {
 
+// M = 1 launch shape: 2 row pairs per wave, 4 waves (8.76-8.84 us at d_ff =
+// 12,288 in a graph-timed sweep, against 9.8-10.1 us for 1 or 4 pairs and 2
+// or 8 waves).
 constexpr int kPairs3 = 2;     // row pairs per wave (M = 1)
 constexpr int kFfn3Waves = 4;  // waves per workgroup (M = 1)
 
@@ -271,11 +274,13 @@ hipError_t launch_swiglu3_gate_up_small(const uint32_t* gate, const float* gate_
                                         const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x,
                                         int m, uint16_t* h, hipStream_t stream) {
   if (m == 1) return launch_swiglu3_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
-  // d_model <= 4,096: at most 16 units of 256 columns.
-  if (d_ff >= 8192 && m == 2) {
+  // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from a
+  // graph-timed sweep on MI355X at d_ff = 12,288 (pools of 36 layers, both
+  // orders): three tiles of 4 waves, 13.2 / 13.4 / 14.4 us at m = 2 / 4 / 8,
+  // within 0.15 us of the best of nine shapes at every m (six tiles of 8
+  // waves, the 2-bit block's shape from m = 3: 13.8 / 14.0 / 14.5 us).
+  if (d_ff >= 8192) {
     launch_gate_up3_mfma<4, 3, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  } else if (d_ff >= 8192) {
-    launch_gate_up3_mfma<8, 6, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   } else {
     launch_gate_up3_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
   }

@@ -64,6 +64,10 @@ def test_lane3_bytes():
     assert weights == 72_351_744
     assert bench.ternary3_bytes(*synth.SHAPES["gate"]) == 12288 * 1536 + 4 * 12288 + 2 * 4096 + 4 * 12288
     assert bench.ternary3_bytes(*synth.SHAPES["down"], 8) == 4096 * 4608 + 4 * 4096 + 8 * (2 * 12288 + 4 * 4096)
+    # the 3-bit block: both 3-bit gate|up matrices and scales, x in, h out; then down on h
+    assert bench.ffn3_block_bytes(synth.HIDDEN, synth.FFN) == (2 * 12288 * 1536 + 2 * 4 * 12288 + 2 * 4096
+                                                               + 2 * 12288 + 4096 * 4608 + 4 * 4096 + 2 * 12288
+                                                               + 4 * 4096) == 56_811_520
 
 
 def test_more_than_one_gpu_is_refused():
