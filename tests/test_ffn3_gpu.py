@@ -12,6 +12,7 @@ the CPU oracle (oracle.ffn3_swiglu) and exact integer arithmetic.
   g and u implies; y within 1e-3 * s_r * sum_j |c_rj| |h_j| of the oracle's down
   linear on the kernel's own h.
 * Repeats and graph replays are bitwise identical to eager calls.
+* d_ff = 2^24 (the largest grid), exact.
 """
 from __future__ import annotations
 
@@ -230,3 +231,39 @@ def test_ffn3_errors(pbg):
     assert lib.ternary3_ffn_swiglu(*args, d_model, d_ff, x.data_ptr() + 8, hbuf.data_ptr(), y.data_ptr(), stream) == -3
     for dm, dff in ((100, d_ff), (4104, d_ff), (0, d_ff), (d_model, 0)):
         assert lib.ternary3_ffn_swiglu(*args, dm, dff, x.data_ptr(), hbuf.data_ptr(), y.data_ptr(), stream) == -2
+
+
+def test_ffn3_max_d_ff(pbg):
+    """d_ff = 2^24 with d_model = 8 (the largest gate/up grid; down is one
+    16M-column row group): integer probe with codes of magnitude 1 and 2 in all
+    three linears, h and y exact."""
+    d_model, d_ff = 8, 1 << 24
+    say(f"ffn3 max d_ff d_model={d_model} d_ff={d_ff}")
+    x = np.array([1, -1, 1, 1, -1, 1, -1, -1], dtype=np.float16)
+    sx = np.where(x > 0, 1, -1).astype(np.int8)
+    # gate rows: sign(x) times 1 or 2 in every column (negated on rows r = 3 mod 5), scale 8, so
+    # g = +-64 or +-128; up rows: one code 1 or 2 times sign(x_j) at column j = r % 8, so u = 1 or 2
+    gmag = np.array([1, 2, 1, 2, 2], dtype=np.int8)
+    gate = gmag[:, None] * sx[None, :]
+    gate[3] = -gate[3]
+    g_codes = torch.from_numpy(gate).to("cuda:0").repeat((d_ff + 4) // 5, 1)[:d_ff].contiguous()
+    rows = torch.arange(d_ff, device="cuda:0")
+    cols = rows % d_model
+    umag = 1 + (rows // d_model) % 2
+    u_codes = torch.zeros((d_ff, d_model), dtype=torch.int8, device="cuda:0")
+    u_codes[rows, cols] = (torch.from_numpy(sx).to("cuda:0")[cols] * umag).to(torch.int8)
+    del rows, cols, umag
+    gs = torch.full((d_ff,), 8.0, dtype=torch.float32, device="cuda:0")
+    us = torch.ones(d_ff, dtype=torch.float32, device="cuda:0")
+    down = synth.ternary3_codes(48, d_model, d_ff, synth.balanced(0.9995))
+    sd = synth.pow2_scales(49, d_model)
+    r = np.arange(d_ff)
+    # silu(64 or 128) is 64 or 128 exactly in fp32; silu(-128) * u rounds to -0 in fp16
+    h_exp = np.where(r % 5 == 3, 0.0, 64.0 * gmag[r % 5] * (1 + (r // d_model) % 2))
+    assert np.all(np.abs(down).astype(np.int64) @ h_exp.astype(np.int64) * 2 < 2 ** 24)  # exact fp32 sums
+    y_exp = (down.astype(np.int64) @ h_exp.astype(np.int64)).astype(np.float64) * sd.astype(np.float64)
+    h, y = pbg.ternary3_ffn_swiglu(pbg.pack_ternary3(g_codes)[0], gs, pbg.pack_ternary3(u_codes)[0], us,
+                                   pack3(pbg, down), dev(sd), dev(x))
+    del g_codes, u_codes
+    assert np.array_equal(h.cpu().numpy().astype(np.float64), h_exp)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_exp)

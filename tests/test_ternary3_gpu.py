@@ -10,6 +10,7 @@ CPU oracle.
   shapes that hit every launch shape and the element-guarded kernel, and on
   seeded workloads within |y - y_ref| <= 1e-3 * s_r * sum_j |c_rj| |x_j|;
   full-size gate and down tensors on sampled rows.
+* Maximum sizes: k = 2^24 and n = 2^24, exact.
 """
 from __future__ import annotations
 
@@ -215,3 +216,50 @@ def test_gemv3_full_size_sampled(pbg, proj):
     assert_within(y[rows][None, :], ref[None, :], ternary3_bound(c_rows, s_rows, x), proj)
     assert np.array_equal(host_words(packed[torch.from_numpy(rows).to("cuda:0")]), oracle.pack3(c_rows)[0])
     assert int(stats[5]) == 0 and int(stats.sum()) == n * k
+
+
+# --------------------------------------------------------------------------
+# Maximum sizes (PBG_MAX_K, PBG_MAX_N): the largest row and the largest grids
+# --------------------------------------------------------------------------
+def test_gemv3_max_k(pbg):
+    """k = 2^24 (6 MiB per row, the element-guarded kernels): exact probe with
+    99 % zeros, so that every fp32 partial sum (in units of 2 c x) stays an
+    exact integer; one activation row and two."""
+    n, k = 3, 1 << 24
+    say(f"gemv3 max k n={n} k={k}")
+    codes = synth.ternary3_codes(41, n, k, synth.balanced(0.99))
+    x = synth.probe_activations(42, 2, k)
+    s = synth.pow2_scales(43, n)
+    assert np.all(np.abs(codes).sum(axis=1, dtype=np.int64) * 8 * 2 < 2 ** 24)
+    ref_p = oracle.pack3(codes)[0]
+    p, _, _ = gpu_pack3(pbg, codes)
+    assert np.array_equal(host_words(p), ref_p)
+    y = pbg.ternary3_gemv(p, dev(s), k, dev(x[0])).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, oracle.ternary3_gemv(ref_p, s, k, x[0]))
+    y2 = pbg.ternary3_gemm_small(p, dev(s), k, dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y2, oracle.ternary3_gemm_small(ref_p, s, k, x))
+
+
+def test_gemv3_max_n(pbg):
+    """n = 2^24 rows (the largest grids of the 3-bit GEMV and of its matrix-core
+    m-row kernel): exact probes on sampled rows, the last rows included."""
+    n, k = 1 << 24, 16
+    say(f"gemv3 max n n={n} k={k}")
+    codes = synth.ternary3_codes_device(44, n, k, synth.GLOBAL_DIST, "cuda:0")
+    x = synth.probe_activations(45, 8, k)
+    s_host = synth.pow2_scales(46, 4096)
+    s = dev(np.resize(s_host, n))  # scales repeat every 4,096 rows
+    p, _, st = pbg.pack_ternary3(codes)
+    assert int(st.cpu()[:5].sum()) == n * k
+    rng = np.random.Generator(np.random.PCG64(47))
+    rows = np.unique(np.concatenate([rng.choice(n, size=4096, replace=False), np.arange(n - 16, n)]))
+    idx = torch.from_numpy(rows).to("cuda:0")
+    c_rows = codes[idx].cpu().numpy()
+    del codes
+    s_rows = s_host[rows % 4096]
+    ref_p = oracle.pack3(c_rows)[0]
+    y = pbg.ternary3_gemv(p, s, k, dev(x[0])).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y[rows], oracle.ternary3_gemv(ref_p, s_rows, k, x[0]))
+    del y
+    y8 = pbg.ternary3_gemm_small(p, s, k, dev(x)).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y8[:, rows], oracle.ternary3_gemm_small(ref_p, s_rows, k, x))
