@@ -543,10 +543,10 @@ def main():
             pbg.ternary_gemm_small(qp, qs, synth.HIDDEN, xs[synth.HIDDEN][:m], yqkv_m[:m])
             linear(l, "o", m)
             lay = model.layers[l]
-            # the block: gate|up + SwiGLU for m rows, then down on h (split over K where that is faster)
-            pbg.ternary_swiglu_gate_up(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], synth.HIDDEN,
-                                       xs[synth.HIDDEN][:m], h_m[:m])
-            pbg.ternary_gemm_splitk(lay["down"][0], lay["down"][1], synth.FFN, h_m[:m], ws_down, y_m[:m])
+            # the block: gate|up + SwiGLU for m rows, then down on h (split over K in two slices added
+            # onto y, which the gate|up launch clears)
+            pbg.ternary_ffn_swiglu(lay["gate"][0], lay["gate"][1], lay["up"][0], lay["up"][1], lay["down"][0],
+                                   lay["down"][1], xs[synth.HIDDEN][:m], h_m[:m], y_m[:m])
 
         for m in (2, 4, 7, 8):
             graphs = [capture(torch, lambda l=l, m=m: fused_layer_m(l, m)) for l in range(L)]

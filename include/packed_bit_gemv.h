@@ -343,6 +343,12 @@ int ternary_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, con
  * d_model, d_ff, the packs and scales are as for the m = 1 calls (same limits
  * and alignment); m = 1 runs exactly the m = 1 kernels. Returns PBG_ERR_SHAPE
  * for m outside [1, PBG_MAX_M].
+ * For 2 <= m with d_ff % 8 == 0 and 4,096 < d_ff <= 12,288, the ffn call
+ * splits down over K in two slices that each add their part to y with an
+ * fp32 atomic add, after the gate|up launch has set y to +0: y's earlier
+ * contents are ignored, and the result is the same bits on every call (two
+ * addends onto +0 give one result in either order). y must not overlap h, x
+ * or the weights.
  */
 int ternary_swiglu_gate_up_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
                                  const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m,

@@ -122,7 +122,7 @@ template <int SK, int T, int UPW, int MP>
 __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
     const uint4* __restrict__ gate, const float* __restrict__ gate_scale, const uint4* __restrict__ up,
     const float* __restrict__ up_scale, int64_t d_model, int64_t d_ff, int64_t chunks, const uint16_t* __restrict__ x,
-    int m, uint16_t* __restrict__ h) {
+    int m, uint16_t* __restrict__ h, float* __restrict__ yz, int64_t yz_n) {
   constexpr int kPairsWg = 8 * T;  // gate/up row pairs of the workgroup
   __shared__ float part[SK][16 * T][8];
   const int lane = threadIdx.x & (kWave - 1);
@@ -224,24 +224,51 @@ __global__ __launch_bounds__(SK* kWave) void swiglu_gate_up_mfma_kernel(
       h[static_cast<int64_t>(j) * d_ff + r] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
     }
   }
+  // the block's y, cleared for the down linear's slices to add onto (yz_n = 0: none)
+  const int64_t nth = static_cast<int64_t>(gridDim.x) * (SK * kWave);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * (SK * kWave) + threadIdx.x; i < yz_n; i += nth) yz[i] = 0.0f;
 }
 
 template <int SK, int T, int UPW, int MP>
 void launch_gate_up_mp(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
-                       int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {
+                       int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* yz,
+                       int64_t yz_n, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((d_ff + 8 * T - 1) / (8 * T)));
   hipLaunchKernelGGL((swiglu_gate_up_mfma_kernel<SK, T, UPW, MP>), grid, dim3(SK * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(gate), gate_scale, reinterpret_cast<const uint4*>(up), up_scale,
-                     d_model, d_ff, words_per_row(d_model) / 4, x, m, h);
+                     d_model, d_ff, words_per_row(d_model) / 4, x, m, h, yz, yz_n);
 }
 
 // MP = m rounded up to 2, 4 or 8: the activation rows one x slice holds.
 template <int SK, int T, int UPW>
 void launch_gate_up_mfma(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
-                         int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {
-  if (m <= 2) launch_gate_up_mp<SK, T, UPW, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  else if (m <= 4) launch_gate_up_mp<SK, T, UPW, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  else launch_gate_up_mp<SK, T, UPW, 8>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+                         int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* yz,
+                         int64_t yz_n, hipStream_t stream) {
+  if (m <= 2) launch_gate_up_mp<SK, T, UPW, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  else if (m <= 4)
+    launch_gate_up_mp<SK, T, UPW, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  else launch_gate_up_mp<SK, T, UPW, 8>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+}
+
+// 2 <= m <= 8: the matrix-core gate|up launch by shape; yz_n > 0 also clears
+// yz[0 .. yz_n).
+hipError_t gate_up_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
+                         int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* yz,
+                         int64_t yz_n, hipStream_t stream) {
+  // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from
+  // graph-timed sweeps on MI355X at d_ff = 12,288 (settled clocks, both
+  // orders): three tiles (24 pairs, 512 workgroups) of 4 waves at m = 2
+  // (7.54 us), six tiles of 8 waves from m = 3 (7.65 / 7.67 / 8.11 us at m =
+  // 3 / 4 / 8, against 7.84-7.87 / 7.87-8.01 / 8.78 for three tiles of 4
+  // waves); four tiles took 9.3-10.6 us in an earlier sweep.
+  if (d_ff >= 8192 && m == 2) {
+    launch_gate_up_mfma<4, 3, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  } else if (d_ff >= 8192) {
+    launch_gate_up_mfma<8, 6, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  } else {
+    launch_gate_up_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  }
+  return hipGetLastError();
 }
 }  // namespace
 
@@ -268,27 +295,24 @@ hipError_t launch_swiglu_gate_up_small(const uint32_t* gate, const float* gate_s
                                        const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x,
                                        int m, uint16_t* h, hipStream_t stream) {
   if (m == 1) return launch_swiglu_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
-  // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from
-  // graph-timed sweeps on MI355X at d_ff = 12,288 (settled clocks, both
-  // orders): three tiles (24 pairs, 512 workgroups) of 4 waves at m = 2
-  // (7.54 us), six tiles of 8 waves from m = 3 (7.65 / 7.67 / 8.11 us at m =
-  // 3 / 4 / 8, against 7.84-7.87 / 7.87-8.01 / 8.78 for three tiles of 4
-  // waves); four tiles took 9.3-10.6 us in an earlier sweep.
-  if (d_ff >= 8192 && m == 2) {
-    launch_gate_up_mfma<4, 3, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  } else if (d_ff >= 8192) {
-    launch_gate_up_mfma<8, 6, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  } else {
-    launch_gate_up_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  }
-  return hipGetLastError();
+  return gate_up_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, nullptr, 0, stream);
 }
 
 hipError_t launch_ffn_swiglu_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
                                    const float* up_scale, const uint32_t* down, const float* down_scale,
                                    int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* y,
                                    hipStream_t stream) {
-  const hipError_t e = launch_swiglu_gate_up_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  if (m == 1) return launch_ffn_swiglu(gate, gate_scale, up, up_scale, down, down_scale, d_model, d_ff, x, h, y, stream);
+  // Down split over K in two slices that add onto y, which the gate|up
+  // launch clears (no workspace and no extra launch).
+  if (ternary_split2_applies(d_model, d_ff, m, h)) {
+    const hipError_t e =
+        gate_up_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, y, static_cast<int64_t>(m) * d_model,
+                      stream);
+    if (e != hipSuccess) return e;
+    return launch_ternary_gemm_split2(down, down_scale, d_model, d_ff, h, m, y, stream);
+  }
+  const hipError_t e = gate_up_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, nullptr, 0, stream);
   if (e != hipSuccess) return e;
   return launch_ternary_gemm_small(down, down_scale, d_model, d_ff, h, m, y, stream);
 }

@@ -25,6 +25,13 @@ hipError_t launch_ternary_gemm_splitk(const uint32_t* packed, const float* scale
                                       const uint16_t* x, int m, float* y, void* ws, int64_t ws_bytes,
                                       hipStream_t stream);
 
+// Small-M GEMM split over K into at most two slices that add s * partial to y
+// with fp32 atomics; y must hold +0 in every element on entry (the FFN block
+// clears it in its gate|up launch). Applies when ternary_split2_applies.
+bool ternary_split2_applies(int64_t n, int64_t k, int m, const uint16_t* x);
+hipError_t launch_ternary_gemm_split2(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                      const uint16_t* x, int m, float* y, hipStream_t stream);
+
 hipError_t launch_int8_head(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x,
                             int m, float* y, hipStream_t stream);
 

@@ -301,10 +301,13 @@ __global__ __launch_bounds__(kGemvWaves* kWave) void ternary_gemm_small_kernel(c
 // j mod MP, conflict-free. Columns j >= M are discarded in the epilogue.
 // A workgroup holds SK waves that split the units of T tiles; their partial
 // tiles meet in LDS and are added in wave order.
-// SPLIT: K is also split across workgroups; blockIdx.y is the slice of
-// SK * UPW units (starting at unit blockIdx.y * SK * UPW), and the slices of
-// a row block meet through `sp` (SplitK).
-template <int SK, int T, int UPW, int MP, bool SPLIT>
+// SPLIT (0 = whole K per workgroup): K is also split across workgroups;
+// blockIdx.y is the slice of SK * UPW units (starting at unit blockIdx.y * SK
+// * UPW). SPLIT = 1: the slices of a row block meet through `sp` (SplitK).
+// SPLIT = 2: at most two slices, each adds s * its partial to y with an fp32
+// atomic add; y holds +0 on entry, and +0 + a + b gives the same bits in
+// either order, so the result does not depend on which slice ends first.
+template <int SK, int T, int UPW, int MP, int SPLIT>
 __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint4* __restrict__ packed,
                                                                        const float* __restrict__ scale,
                                                                        int64_t n, int64_t k, int64_t chunks,
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
   const int li = lane & 15, lg = lane >> 4;
   const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kRows;
   const int64_t groups = k / 8;  // 8-column activation groups
-  const int64_t u0 = SPLIT ? static_cast<int64_t>(blockIdx.y) * SK * UPW : 0;  // first unit of the slice
+  const int64_t u0 = SPLIT != 0 ? static_cast<int64_t>(blockIdx.y) * SK * UPW : 0;  // first unit of the slice
   const uint4* xg = reinterpret_cast<const uint4*>(x);
 
   // Outputs (row, column) o = threadIdx.x + e * SK * 64 of the tile block,
@@ -409,10 +412,13 @@ __global__ __launch_bounds__(SK* kWave) void ternary_gemm_mfma_kernel(const uint
       sum[e] = part[0][orow][ocol];
 #pragma unroll
       for (int w = 1; w < SK; ++w) sum[e] += part[w][orow][ocol];
-      if constexpr (!SPLIT) y[static_cast<int64_t>(ocol) * n + r] = sum[e] * (sc[e] * kCodeUnitInv);
+      if constexpr (SPLIT == 0) y[static_cast<int64_t>(ocol) * n + r] = sum[e] * (sc[e] * kCodeUnitInv);
+      if constexpr (SPLIT == 2)
+        __hip_atomic_fetch_add(y + static_cast<int64_t>(ocol) * n + r, sum[e] * (sc[e] * kCodeUnitInv),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT == 1) {
     unsigned long long* acc = sp.acc + static_cast<int64_t>(blockIdx.x) * (kRows * 8);
 #pragma unroll
     for (int e = 0; e < kOut; ++e) {
@@ -438,7 +444,7 @@ template <int SK, int T, int UPW, int MP>
 void launch_mfma_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x, int m,
                     float* y, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
-  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP, false>), grid, dim3(SK * kWave), 0, stream,
+  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP, 0>), grid, dim3(SK * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y,
                      SplitK{nullptr, 1});
 }
@@ -470,7 +476,7 @@ hipError_t launch_mfma_split_mp(const uint32_t* packed, const float* scale, int6
   const int64_t nrb = (n + 16 * T - 1) / (16 * T);
   const int slices = static_cast<int>((units + SK * UPW - 1) / (SK * UPW));
   if (slices > 15 || 8 * nrb * (16 * T * 8) > ws_bytes) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP, true>), dim3(static_cast<unsigned>(nrb), slices),
+  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP, 1>), dim3(static_cast<unsigned>(nrb), slices),
                      dim3(SK * kWave), 0, stream, reinterpret_cast<const uint4*>(packed), scale, n, k,
                      words_per_row(k) / 4, x, m, y, SplitK{static_cast<unsigned long long*>(ws), slices});
   return hipGetLastError();
@@ -484,7 +490,35 @@ hipError_t launch_mfma_split(const uint32_t* packed, const float* scale, int64_t
   return launch_mfma_split_mp<SK, T, UPW, 8>(packed, scale, n, k, x, m, y, ws, ws_bytes, stream);
 }
 
+// Two K-slices added onto a zeroed y (SPLIT = 2).
+template <int SK, int T, int UPW, int MP>
+void launch_mfma_split2_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, const uint16_t* x,
+                           int m, float* y, hipStream_t stream) {
+  const int64_t units = (words_per_row(k) / 4 + 3) / 4;
+  const unsigned slices = static_cast<unsigned>((units + SK * UPW - 1) / (SK * UPW));
+  hipLaunchKernelGGL((ternary_gemm_mfma_kernel<SK, T, UPW, MP, 2>),
+                     dim3(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)), slices), dim3(SK * kWave), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), scale, n, k, words_per_row(k) / 4, x, m, y,
+                     SplitK{nullptr, static_cast<int>(slices)});
+}
+
 }  // namespace
+
+bool ternary_split2_applies(int64_t n, int64_t k, int m, const uint16_t* x) {
+  const int64_t units = (words_per_row(k) / 4 + 3) / 4;  // 256-column units
+  return k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && m >= 2 && m <= 8 && units > 16 &&
+         units <= 48 && n > 0;
+}
+
+hipError_t launch_ternary_gemm_split2(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                      const uint16_t* x, int m, float* y, hipStream_t stream) {
+  if (!ternary_split2_applies(n, k, m, x)) return hipErrorInvalidValue;
+  // 32-row blocks, 8 waves of 3 units: slices of 24 units (6,144 columns)
+  if (m <= 2) launch_mfma_split2_mp<8, 2, 3, 2>(packed, scale, n, k, x, m, y, stream);
+  else if (m <= 4) launch_mfma_split2_mp<8, 2, 3, 4>(packed, scale, n, k, x, m, y, stream);
+  else launch_mfma_split2_mp<8, 2, 3, 8>(packed, scale, n, k, x, m, y, stream);
+  return hipGetLastError();
+}
 
 int64_t splitk_workspace_bytes(int64_t n, int64_t /*k*/) {
   // one 8-byte accumulator per output of a row block (at most 8 activation

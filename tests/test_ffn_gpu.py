@@ -214,7 +214,7 @@ def test_ffn_errors(pbg):
 # --------------------------------------------------------------------------
 # The block for 2 <= m <= 8 activation rows (speculative verify)
 # --------------------------------------------------------------------------
-SMALL_SHAPES = [(64, 64), (128, 4160), (256, 1024), (192, 12288 + 64), (4096, 12288)]
+SMALL_SHAPES = [(64, 64), (128, 4160), (256, 1024), (96, 8200), (192, 12288 + 64), (4096, 12288)]
 
 
 @pytest.mark.parametrize("m", [2, 3, 5, 8])
@@ -299,3 +299,31 @@ def test_ffn_small_graph_replay(pbg):
         h_e, y_e = pbg.ternary_ffn_swiglu(*args, x)
         torch.cuda.synchronize()
         assert torch.equal(h, h_e) and torch.equal(y, y_e), rep
+
+
+@pytest.mark.parametrize("m", [2, 8])
+@pytest.mark.parametrize("d_model,d_ff", [(4096, 12288), (96, 8200), (128, 4160)])
+def test_ffn_small_y_contents_ignored(pbg, m, d_model, d_ff):
+    """The block's down linear adds its K-slices onto y after the gate|up launch
+    has cleared it: whatever y held before (NaN here) does not reach the result,
+    and repeated calls give the same bits."""
+    say(f"ffn small y reuse m={m} d_model={d_model} d_ff={d_ff}")
+    layer = 2
+    gate = synth.ternary_codes(synth.tensor_seed(layer, "gate") + d_ff, d_ff, d_model, synth.code_dist(layer, "gate"))
+    up = synth.ternary_codes(synth.tensor_seed(layer, "up") + d_ff, d_ff, d_model, synth.code_dist(layer, "up"))
+    down = synth.ternary_codes(synth.tensor_seed(layer, "down") + d_ff, d_model, d_ff,
+                               synth.code_dist(layer, "down"))
+    sg, su, sd = synth.row_scales(621, d_ff), synth.row_scales(622, d_ff), synth.row_scales(623, d_model)
+    x = dev(synth.activations(synth.x_seed(1), m, d_model))
+    args = (pack(pbg, gate), dev(sg), pack(pbg, up), dev(su), pack(pbg, down), dev(sd))
+    h0, y0 = pbg.ternary_ffn_swiglu(*args, x)
+    h = torch.empty_like(h0)
+    y = torch.full_like(y0, float("nan"))
+    for _ in range(3):
+        pbg.ternary_ffn_swiglu(*args, x, h, y)
+        assert torch.equal(h, h0) and torch.equal(y, y0)
+        y.fill_(float("nan"))
+    h_gpu = h0.cpu().numpy()
+    y_down = oracle.ternary_gemm_small(oracle.pack(down)[0], sd, d_ff, h_gpu)
+    assert_within(y0.cpu().numpy(), y_down, ternary_bound(sd, h_gpu), "y = down h")
+
