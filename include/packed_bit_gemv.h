@@ -374,8 +374,9 @@ int ternary_ffn_swiglu_small(const uint32_t* gate_packed, const float* gate_scal
  *                           16-byte aligned
  *   down_packed             [d_model][pbg_words_per_row3(d_ff)] uint32,
  *                           16-byte aligned
- * Everything else (scales, x, h, y, m, limits, alignment, return codes) is as
- * for the 2-bit calls of the same name without the 3.
+ * Everything else (scales, x, h, y, m, limits, alignment, return codes, and
+ * the two K-slices of down added onto a cleared y for 2 <= m) is as for the
+ * 2-bit calls of the same name without the 3.
  */
 int ternary3_swiglu_gate_up(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
                             const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, uint16_t* h,

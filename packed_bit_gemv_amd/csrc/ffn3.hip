@@ -127,7 +127,7 @@ template <int SK, int T, int UPW, int MP>
 __global__ __launch_bounds__(SK* kWave) void swiglu3_gate_up_mfma_kernel(
     const uint32_t* __restrict__ gate, const float* __restrict__ gate_scale, const uint32_t* __restrict__ up,
     const float* __restrict__ up_scale, int64_t d_model, int64_t d_ff, int64_t chunks, const uint16_t* __restrict__ x,
-    int m, uint16_t* __restrict__ h) {
+    int m, uint16_t* __restrict__ h, float* __restrict__ yz, int64_t yz_n) {
   constexpr int kPairsWg = 8 * T;  // gate/up row pairs of the workgroup
   __shared__ float part[SK][16 * T][8];
   const int lane = threadIdx.x & (kWave - 1);
@@ -232,23 +232,48 @@ __global__ __launch_bounds__(SK* kWave) void swiglu3_gate_up_mfma_kernel(
       h[static_cast<int64_t>(j) * d_ff + r] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv));
     }
   }
+  // the block's y, cleared for the down linear's slices to add onto (yz_n = 0: none)
+  const int64_t nth = static_cast<int64_t>(gridDim.x) * (SK * kWave);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * (SK * kWave) + threadIdx.x; i < yz_n; i += nth) yz[i] = 0.0f;
 }
 
 template <int SK, int T, int UPW, int MP>
 void launch_gate_up3_mp(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
-                        int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {
+                        int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* yz, int64_t yz_n,
+                        hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((d_ff + 8 * T - 1) / (8 * T)));
   hipLaunchKernelGGL((swiglu3_gate_up_mfma_kernel<SK, T, UPW, MP>), grid, dim3(SK * kWave), 0, stream, gate,
-                     gate_scale, up, up_scale, d_model, d_ff, words_per_row3(d_model) / 6, x, m, h);
+                     gate_scale, up, up_scale, d_model, d_ff, words_per_row3(d_model) / 6, x, m, h, yz, yz_n);
 }
 
 // MP = m rounded up to 2, 4 or 8.
 template <int SK, int T, int UPW>
 void launch_gate_up3_mfma(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
-                          int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, hipStream_t stream) {
-  if (m <= 2) launch_gate_up3_mp<SK, T, UPW, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  else if (m <= 4) launch_gate_up3_mp<SK, T, UPW, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  else launch_gate_up3_mp<SK, T, UPW, 8>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+                          int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* yz,
+                          int64_t yz_n, hipStream_t stream) {
+  if (m <= 2)
+    launch_gate_up3_mp<SK, T, UPW, 2>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  else if (m <= 4)
+    launch_gate_up3_mp<SK, T, UPW, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  else launch_gate_up3_mp<SK, T, UPW, 8>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+}
+
+// 2 <= m <= 8: the matrix-core gate|up launch by shape; yz_n > 0 also clears
+// yz[0 .. yz_n).
+hipError_t gate_up3_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up, const float* up_scale,
+                          int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* yz,
+                          int64_t yz_n, hipStream_t stream) {
+  // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from a
+  // graph-timed sweep on MI355X at d_ff = 12,288 (pools of 36 layers, both
+  // orders): three tiles of 4 waves, 13.2 / 13.4 / 14.4 us at m = 2 / 4 / 8,
+  // within 0.15 us of the best of nine shapes at every m (six tiles of 8
+  // waves, the 2-bit block's shape from m = 3: 13.8 / 14.0 / 14.5 us).
+  if (d_ff >= 8192) {
+    launch_gate_up3_mfma<4, 3, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  } else {
+    launch_gate_up3_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, yz, yz_n, stream);
+  }
+  return hipGetLastError();
 }
 }  // namespace
 
@@ -274,24 +299,24 @@ hipError_t launch_swiglu3_gate_up_small(const uint32_t* gate, const float* gate_
                                         const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x,
                                         int m, uint16_t* h, hipStream_t stream) {
   if (m == 1) return launch_swiglu3_gate_up(gate, gate_scale, up, up_scale, d_model, d_ff, x, h, stream);
-  // d_model <= 4,096: at most 16 units of 256 columns. Launch shapes from a
-  // graph-timed sweep on MI355X at d_ff = 12,288 (pools of 36 layers, both
-  // orders): three tiles of 4 waves, 13.2 / 13.4 / 14.4 us at m = 2 / 4 / 8,
-  // within 0.15 us of the best of nine shapes at every m (six tiles of 8
-  // waves, the 2-bit block's shape from m = 3: 13.8 / 14.0 / 14.5 us).
-  if (d_ff >= 8192) {
-    launch_gate_up3_mfma<4, 3, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  } else {
-    launch_gate_up3_mfma<4, 2, 4>(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
-  }
-  return hipGetLastError();
+  return gate_up3_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, nullptr, 0, stream);
 }
 
 hipError_t launch_ffn3_swiglu_small(const uint32_t* gate, const float* gate_scale, const uint32_t* up,
                                     const float* up_scale, const uint32_t* down, const float* down_scale,
                                     int64_t d_model, int64_t d_ff, const uint16_t* x, int m, uint16_t* h, float* y,
                                     hipStream_t stream) {
-  const hipError_t e = launch_swiglu3_gate_up_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, stream);
+  if (m == 1)
+    return launch_ffn3_swiglu(gate, gate_scale, up, up_scale, down, down_scale, d_model, d_ff, x, h, y, stream);
+  // as the 2-bit block: down split over K in two slices that add onto y,
+  // which the gate|up launch clears
+  if (ternary3_split2_applies(d_model, d_ff, m, h)) {
+    const hipError_t e = gate_up3_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, y,
+                                        static_cast<int64_t>(m) * d_model, stream);
+    if (e != hipSuccess) return e;
+    return launch_ternary3_gemm_split2(down, down_scale, d_model, d_ff, h, m, y, stream);
+  }
+  const hipError_t e = gate_up3_small(gate, gate_scale, up, up_scale, d_model, d_ff, x, m, h, nullptr, 0, stream);
   if (e != hipSuccess) return e;
   return launch_ternary3_gemm_small(down, down_scale, d_model, d_ff, h, m, y, stream);
 }

@@ -81,6 +81,10 @@ hipError_t launch_ternary3_gemv(const uint32_t* packed, const float* scale, int6
                                 float* y, hipStream_t stream);
 hipError_t launch_ternary3_gemm_small(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
                                       const uint16_t* x, int m, float* y, hipStream_t stream);
+// The 3-bit form of ternary_split2_applies / launch_ternary_gemm_split2 (y +0 on entry).
+bool ternary3_split2_applies(int64_t n, int64_t k, int m, const uint16_t* x);
+hipError_t launch_ternary3_gemm_split2(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                       const uint16_t* x, int m, float* y, hipStream_t stream);
 
 // The SwiGLU block with 3-bit linears (d_model <= PBG_FFN_MAX_MODEL, 16-byte aligned x and h).
 hipError_t launch_swiglu3_gate_up(const uint32_t* gate, const float* gate_scale, const uint32_t* up,

@@ -270,7 +270,11 @@ __global__ __launch_bounds__(4 * kWave) void ternary3_generic_kernel(const uint3
 // waves splitting the 256-column units of T tiles) with the magnitude bits
 // OR-ed into every A operand. Lane (i, g) loads, per unit, sign/nonzero chunk
 // 4u + g of its row (16 bytes) and that chunk's two magnitude words.
-template <int SK, int T, int UPW, int MP>
+// SPLIT2: K is also split across workgroups into at most two slices of SK *
+// UPW units (blockIdx.y, as in the 2-bit kernel's SPLIT = 2): each adds s *
+// its partial to y, which holds +0 on entry, with an fp32 atomic add; two
+// addends onto +0 give the same bits in either order.
+template <int SK, int T, int UPW, int MP, bool SPLIT2>
 __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uint32_t* __restrict__ packed,
                                                                         const float* __restrict__ scale, int64_t n,
                                                                         int64_t k, int64_t chunks,
@@ -284,6 +288,7 @@ __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uin
   const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kRows;
   const int64_t groups = k / 8;
   const int64_t row_words = 6 * chunks;
+  const int64_t u0 = SPLIT2 ? static_cast<int64_t>(blockIdx.y) * SK * UPW : 0;  // first unit of the slice
   const uint4* xg = reinterpret_cast<const uint4*>(x);
 
   constexpr int kOut = (kRows * 8 + SK * kWave - 1) / (SK * kWave);
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uin
   __shared__ uint4 xs[SK][2][MP * kSlots];
   const int xrow = li >> 3, xg8 = li & 7;
   auto load_x = [&](int q, uint4 (&xr)[kXLoads]) {
-    const int64_t u = s + static_cast<int64_t>(SK) * q;
+    const int64_t u = u0 + s + static_cast<int64_t>(SK) * q;
 #pragma unroll
     for (int a = 0; a < kXLoads; ++a) {
       const int row = 2 * a + xrow;
@@ -309,13 +314,13 @@ __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uin
     }
   };
   auto stage_x = [&](int q, const uint4 (&xr)[kXLoads]) {
-    const int64_t gi = 32 * (s + static_cast<int64_t>(SK) * q) + 8 * lg + xg8;
+    const int64_t gi = 32 * (u0 + s + static_cast<int64_t>(SK) * q) + 8 * lg + xg8;
 #pragma unroll
     for (int a = 0; a < kXLoads; ++a)
       xs[s][q & 1][(2 * a + xrow) * kSlots + 8 * lg + xg8] = masked(xr[a], gi < groups);
   };
   auto load_w = [&](int q, uint4 (&wv)[T], uint2 (&mv)[T]) {
-    const int64_t c = 4 * (s + static_cast<int64_t>(SK) * q) + lg;
+    const int64_t c = 4 * (u0 + s + static_cast<int64_t>(SK) * q) + lg;
     const int64_t cc = c < chunks ? c : chunks - 1;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -368,7 +373,11 @@ __global__ __launch_bounds__(SK* kWave) void ternary3_gemm_mfma_kernel(const uin
       float sum = part[0][orow][ocol];
 #pragma unroll
       for (int w = 1; w < SK; ++w) sum += part[w][orow][ocol];
-      y[static_cast<int64_t>(ocol) * n + r] = sum * (sc[e] * kCodeUnitInv);
+      if constexpr (SPLIT2)
+        __hip_atomic_fetch_add(y + static_cast<int64_t>(ocol) * n + r, sum * (sc[e] * kCodeUnitInv),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        y[static_cast<int64_t>(ocol) * n + r] = sum * (sc[e] * kCodeUnitInv);
     }
   }
 }
@@ -377,8 +386,19 @@ template <int SK, int T, int UPW, int MP>
 void launch_mfma3_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, int64_t chunks,
                      const uint16_t* x, int m, float* y, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)));
-  hipLaunchKernelGGL((ternary3_gemm_mfma_kernel<SK, T, UPW, MP>), grid, dim3(SK * kWave), 0, stream, packed, scale,
-                     n, k, chunks, x, m, y);
+  hipLaunchKernelGGL((ternary3_gemm_mfma_kernel<SK, T, UPW, MP, false>), grid, dim3(SK * kWave), 0, stream, packed,
+                     scale, n, k, chunks, x, m, y);
+}
+
+// Two K-slices added onto a zeroed y.
+template <int SK, int T, int UPW, int MP>
+void launch_mfma3_split2_mp(const uint32_t* packed, const float* scale, int64_t n, int64_t k, int64_t chunks,
+                            const uint16_t* x, int m, float* y, hipStream_t stream) {
+  const int64_t units = (chunks + 3) / 4;
+  const unsigned slices = static_cast<unsigned>((units + SK * UPW - 1) / (SK * UPW));
+  hipLaunchKernelGGL((ternary3_gemm_mfma_kernel<SK, T, UPW, MP, true>),
+                     dim3(static_cast<unsigned>((n + 16 * T - 1) / (16 * T)), slices), dim3(SK * kWave), 0, stream,
+                     packed, scale, n, k, chunks, x, m, y);
 }
 
 template <int SK, int T, int UPW>
@@ -446,6 +466,23 @@ hipError_t launch_ternary3_gemv(const uint32_t* packed, const float* scale, int6
       else launch_gemv3_cfg<4, 4, 1>(packed, scale, n, k, chunks, x, y, stream);
       break;
   }
+  return hipGetLastError();
+}
+
+bool ternary3_split2_applies(int64_t n, int64_t k, int m, const uint16_t* x) {
+  const int64_t units = (words_per_row3(k) / 6 + 3) / 4;  // 256-column units
+  return k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && m >= 2 && m <= 8 && units > 16 &&
+         units <= 48 && n > 0;
+}
+
+hipError_t launch_ternary3_gemm_split2(const uint32_t* packed, const float* scale, int64_t n, int64_t k,
+                                       const uint16_t* x, int m, float* y, hipStream_t stream) {
+  if (!ternary3_split2_applies(n, k, m, x)) return hipErrorInvalidValue;
+  const int64_t chunks = words_per_row3(k) / 6;
+  // the 2-bit block's shape: 32-row blocks, 8 waves of 3 units, slices of 24 units
+  if (m <= 2) launch_mfma3_split2_mp<8, 2, 3, 2>(packed, scale, n, k, chunks, x, m, y, stream);
+  else if (m <= 4) launch_mfma3_split2_mp<8, 2, 3, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+  else launch_mfma3_split2_mp<8, 2, 3, 8>(packed, scale, n, k, chunks, x, m, y, stream);
   return hipGetLastError();
 }
 
