@@ -150,3 +150,36 @@ def swiglu_h_bound(silu_g: np.ndarray, u: np.ndarray, tg: np.ndarray, tu: np.nda
     mag = np.abs(silu_g * u) + a
     ulp = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(mag, 2.0 ** -14))) - 10), 2.0 ** -24)
     return a + ulp
+
+
+def digit_probes(k: int, base: int) -> tuple[np.ndarray, int]:
+    """Read-back activations: the codes of a row are balanced base-`base`
+    digits (-(base-1)/2 .. (base-1)/2), so with x = base^i on the `nd` columns
+    of one block (zero elsewhere) y_r is the integer whose digits are the
+    block's codes. nd is the largest count whose powers stay fp16-exact
+    integers (3^6 = 729, 5^4 = 625) and whose sums stay below 2^11. Returns
+    (x [blocks, k] fp16, nd); block b covers columns nd*b .. nd*b + nd - 1."""
+    nd = {3: 7, 5: 5}[base]
+    blocks = (k + nd - 1) // nd
+    x = np.zeros((blocks, k), dtype=np.float16)
+    for b in range(blocks):
+        for i in range(nd):
+            if nd * b + i < k:
+                x[b, nd * b + i] = float(base ** i)
+    return x, nd
+
+
+def read_digits(y: np.ndarray, base: int, nd: int, k: int) -> np.ndarray:
+    """Inverse of digit_probes: y [blocks, n] (exact integers, unit scale) ->
+    codes [n, k] as int8, digit i of block b being column nd*b + i."""
+    half = (base - 1) // 2
+    v = np.rint(y).astype(np.int64)
+    assert np.array_equal(v.astype(np.float64), np.asarray(y, dtype=np.float64)), "not an integer"
+    blocks, n = v.shape
+    out = np.zeros((n, blocks * nd), dtype=np.int8)
+    for i in range(nd):
+        d = (v + half) % base - half
+        out[:, i::nd] = d.T
+        v = (v - d) // base
+    assert not v.any(), "more digits than a block holds"
+    return out[:, :k]

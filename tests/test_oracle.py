@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import read_format3_words, read_format_words, read_key_values
+from helpers import digit_probes, read_digits, read_format3_words, read_format_words, read_key_values
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -226,6 +226,28 @@ def test_oracle_rejects_non_finite_activations():
     x[7] = -big
     y = oracle.ternary_gemv(oracle.pack(np.ones((n, k), dtype=np.int8))[0], s, k, x)
     assert np.all(y == (k - 2) * 65504.0)
+
+
+def test_digit_readback_recovers_codes():
+    """The arithmetic path gives every code back: with x = 3^i on the 7
+    columns of one block (zero elsewhere) and unit scales, y_r is that block's
+    codes as a balanced-ternary integer, so reading the digits of y over all
+    blocks must return the code matrix (a wrong code, sign, bit position or
+    column anywhere changes a digit). The five-level codes read back the same
+    way in balanced base 5 on blocks of 5 columns."""
+    n = 23
+    s = np.ones(n, dtype=np.float32)
+    for k in (7, 60, 130):
+        codes = synth.ternary_codes(61 + k, n, k)
+        x, nd = digit_probes(k, 3)
+        packed = oracle.pack(codes)[0]
+        y = np.concatenate([oracle.ternary_gemm_small(packed, s, k, x[b:b + 8]) for b in range(0, len(x), 8)])
+        assert np.array_equal(read_digits(y, 3, nd, k), codes)
+        codes3 = synth.ternary3_codes(71 + k, n, k)
+        x5, nd5 = digit_probes(k, 5)
+        packed3 = oracle.pack3(codes3)[0]
+        y5 = np.concatenate([oracle.ternary3_gemm_small(packed3, s, k, x5[b:b + 8]) for b in range(0, len(x5), 8)])
+        assert np.array_equal(read_digits(y5, 5, nd5, k), codes3)
 
 
 def test_integer_probe_exact():

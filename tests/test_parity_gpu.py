@@ -20,7 +20,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_within, head_bound, ternary_bound
+from helpers import assert_within, digit_probes, head_bound, read_digits, ternary_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -208,6 +208,25 @@ def test_gemv_special_cases(pbg):
     y = pbg.ternary_gemv(gpu_pack(pbg, codes)[0], sd, k, xd).cpu().numpy()
     yn = pbg.ternary_gemv(gpu_pack(pbg, -codes)[0], sd, k, xd).cpu().numpy()
     assert np.array_equal(yn, -y)
+
+
+@pytest.mark.parametrize("n,k", [(37, 56), (300, 4100), (1000, 12288)])
+def test_digit_readback(pbg, n, k):
+    """Every code read back through the kernels' arithmetic: x = 3^i on the 7
+    columns of one block and unit scales make y_r that block's codes as a
+    balanced-ternary integer; over all blocks the digits must equal the codes,
+    through ternary_gemv (one block per call) and ternary_gemm_small (8 blocks,
+    and the remainder, per call)."""
+    say(f"digit readback n={n} k={k}")
+    codes = synth.ternary_codes(2300 + n + k, n, k)
+    packed, _, _ = gpu_pack(pbg, codes)
+    s = dev(np.ones(n, dtype=np.float32))
+    x, nd = digit_probes(k, 3)
+    xd = dev(x)
+    y1 = torch.stack([pbg.ternary_gemv(packed, s, k, xd[b]) for b in range(len(x))]).cpu().numpy()
+    assert np.array_equal(read_digits(y1, 3, nd, k), codes)
+    y8 = torch.cat([pbg.ternary_gemm_small(packed, s, k, xd[b:b + 8]) for b in range(0, len(x), 8)]).cpu().numpy()
+    assert np.array_equal(read_digits(y8, 3, nd, k), codes)
 
 
 def test_gemv_full_size_sampled(pbg):

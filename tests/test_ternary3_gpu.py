@@ -21,7 +21,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_within, read_format3_words, ternary3_bound
+from helpers import assert_within, digit_probes, read_digits, read_format3_words, ternary3_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -195,6 +195,24 @@ def test_gemv3_ternary_codes_match_2bit(pbg):
         y2 = pbg.ternary_gemv(pbg.pack_ternary(codes)[0], s, k, x)
         y3 = pbg.ternary3_gemv(pbg.pack_ternary3(codes)[0], s, k, x)
         assert torch.equal(y2, y3), proj
+
+
+@pytest.mark.parametrize("n,k", [(37, 56), (300, 4100), (1000, 12288)])
+def test_gemv3_digit_readback(pbg, n, k):
+    """Every five-level code read back through the kernels' arithmetic: x =
+    5^i on the 5 columns of one block and unit scales make y_r that block's
+    codes as a balanced base-5 integer; over all blocks the digits must equal
+    the codes, through ternary3_gemv and ternary3_gemm_small."""
+    say(f"digit readback 3-bit n={n} k={k}")
+    codes = synth.ternary3_codes(2400 + n + k, n, k)
+    packed, _, _ = gpu_pack3(pbg, codes)
+    s = dev(np.ones(n, dtype=np.float32))
+    x, nd = digit_probes(k, 5)
+    xd = dev(x)
+    y1 = torch.stack([pbg.ternary3_gemv(packed, s, k, xd[b]) for b in range(len(x))]).cpu().numpy()
+    assert np.array_equal(read_digits(y1, 5, nd, k), codes)
+    y8 = torch.cat([pbg.ternary3_gemm_small(packed, s, k, xd[b:b + 8]) for b in range(0, len(x), 8)]).cpu().numpy()
+    assert np.array_equal(read_digits(y8, 5, nd, k), codes)
 
 
 @pytest.mark.parametrize("proj", ["gate", "down"])
