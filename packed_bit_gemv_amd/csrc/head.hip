@@ -553,10 +553,13 @@ void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, 
   if (aligned && M == 1) {
     launch_head_fast<1, 4, 2, 8, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M == 2) {
-    // two activation rows still fit the VALU path: 101.9 us against 106.8 us
-    // for the persistent matrix-core kernel on the 151,936 x 4,096 head (from
-    // M = 3 the VALU path loses, 128 against 108 us)
-    launch_head_fast<2, 4, 2, 4, AM>(w, scale, n, k, x, y, keys, stream);
+    // two activation rows still fit the VALU path. One group of 8 rows per
+    // 4-wave workgroup streams the 151,936 x 4,096 head at the rate of a
+    // plain read: 91.0 us, against 99.1-99.9 us for two groups of 4 rows and
+    // 106.8 us for the persistent matrix-core kernel (graph-timed sweep of
+    // six shapes). From M = 3 every VALU shape loses to the persistent kernel
+    // (best 111.8 against 108.4 us at M = 3, 120.8 against 109.8 at M = 4).
+    launch_head_fast<2, 4, 1, 8, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && k % kPKStep == 0 && k <= kPMaxK) {
     launch_head_persist<M, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M >= 3 && units <= 8 * 16) {
