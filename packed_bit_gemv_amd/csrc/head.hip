@@ -551,11 +551,12 @@ void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, 
                        (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   const int64_t units = (k / 16 + 3) / 4;  // 64-column units
   if (aligned && M == 1) {
-    // two groups of 4 rows per 8-wave workgroup: 85.4-85.6 us on the 151,936 x
-    // 4,096 head (7.3 TB/s), against 92.2-92.8 us for two groups of 8 rows and
-    // 90.9-91.6 us for the plain read of its bytes; the greedy argmax 90.7-91.4
-    // against 94.1-94.7 us (graph-timed sweep of eight row groupings)
-    launch_head_fast<1, 4, 2, 4, AM>(w, scale, n, k, x, y, keys, stream);
+    // two groups of 8 rows per 8-wave workgroup. Two groups of 4 rows took
+    // 85.4-86.6 against 92.2-93.1 us when timed on their own, but inside the
+    // benchmark's sequence 93.9-100.5 against 90.8-91.5 us (greedy argmax:
+    // 106.5-107.7 against 95.6-97.5 us) with the decode step unchanged, so
+    // the 8-row groups stay.
+    launch_head_fast<1, 4, 2, 8, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M == 2) {
     // two activation rows still fit the VALU path. One group of 8 rows per
     // 4-wave workgroup streams the 151,936 x 4,096 head at the rate of a
