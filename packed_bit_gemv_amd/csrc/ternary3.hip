@@ -494,7 +494,13 @@ hipError_t launch_ternary3_gemm_small(const uint32_t* packed, const float* scale
   if (k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && units <= 64) {
     // The 2-bit small-M launch shapes (ternary.hip), by rows and units.
     if (units <= 16) {
-      if (n >= 8192) launch_mfma3_cfg<4, 3, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+      // N >= 8,192 from a graph-timed sweep of ten shapes at 12,288 x 4,096
+      // (pools of 36 matrices, both orders): one tile of 4 waves at m = 2
+      // (7.40 against 7.70 us for three tiles), three tiles of 8 waves from m
+      // = 3 (7.83 / 8.15 against 7.94 / 8.33 us at m = 4 / 8); the other
+      // shapes of this table were the fastest or within 0.05 us of it
+      if (n >= 8192 && m == 2) launch_mfma3_cfg<4, 1, 4>(packed, scale, n, k, chunks, x, m, y, stream);
+      else if (n >= 8192) launch_mfma3_cfg<8, 3, 2>(packed, scale, n, k, chunks, x, m, y, stream);
       else if (n >= 5120) launch_mfma3_cfg<4, 2, 4>(packed, scale, n, k, chunks, x, m, y, stream);
       else launch_mfma3_cfg<8, 1, 2>(packed, scale, n, k, chunks, x, m, y, stream);
     } else if (units <= 32) {
