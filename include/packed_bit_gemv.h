@@ -347,8 +347,9 @@ int ternary_ffn_swiglu(const uint32_t* gate_packed, const float* gate_scale, con
  * splits down over K in two slices that each add their part to y with an
  * fp32 atomic add, after the gate|up launch has set y to +0: y's earlier
  * contents are ignored, and the result is the same bits on every call (two
- * addends onto +0 give one result in either order). y must not overlap h, x
- * or the weights.
+ * addends onto +0 give one result in either order). y must be device memory
+ * of this GPU (device-scope atomics) and must not overlap h, x or the
+ * weights.
  */
 int ternary_swiglu_gate_up_small(const uint32_t* gate_packed, const float* gate_scale, const uint32_t* up_packed,
                                  const float* up_scale, int64_t d_model, int64_t d_ff, const uint16_t* x, int64_t m,
