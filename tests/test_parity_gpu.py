@@ -700,7 +700,8 @@ def test_ffn_max_d_ff(pbg):
 def test_concurrent_streams_and_threads_match_sequential(pbg):
     """Calls on two streams at once, and from two host threads with a stream
     each, give the same bits as the same calls one after another (every
-    kernel sums in a fixed order, and the argmax workspaces are per caller)."""
+    kernel sums in a fixed order, the argmax workspaces are per caller, and
+    the FFN block's two-slice down adds only onto the caller's own y)."""
     import threading
 
     say("concurrent streams")
@@ -712,14 +713,18 @@ def test_concurrent_streams_and_threads_match_sequential(pbg):
     hw = synth.head_weights_device(synth.SEED_HEAD + 2, hn, k, "cuda:0")
     hs = synth.row_scales_device(synth.SEED_HEAD + 2, hn, "cuda:0")
     x = dev(synth.activations(700, 8, k))
+    codes = synth.ternary_codes_device(synth.tensor_seed(2, "down"), k, n, synth.code_dist(2, "down"), "cuda:0")
+    down = pbg.pack_ternary(codes)[0]
+    del codes
+    sd = synth.row_scales_device(synth.tensor_seed(2, "down"), k, "cuda:0")
 
     def work_a():
         return (pbg.ternary_gemv(packed, s, k, x[0]), pbg.ternary_gemm_small(packed, s, k, x[:4]),
-                pbg.int8_head_gemv(hw, hs, x[:3]))
+                pbg.int8_head_gemv(hw, hs, x[:3]), pbg.ternary_ffn_swiglu(packed, s, packed, s, down, sd, x[:4]))
 
     def work_b(keys):
         return (pbg.int8_head_argmax(hw, hs, x[:7], keys=keys), pbg.ternary_gemm_small(packed, s, k, x[:2]),
-                pbg.int8_head_gemv(hw, hs, x[:1]))
+                pbg.int8_head_gemv(hw, hs, x[:1]), pbg.ternary_ffn_swiglu(packed, s, packed, s, down, sd, x[:8]))
 
     keys_a = torch.zeros(8 * pbg.binding.ARGMAX_KEYS_PER_ROW, dtype=torch.int64, device="cuda:0")
     keys_b = torch.zeros_like(keys_a)
