@@ -131,8 +131,25 @@ def capture(torch, fn):
     return g
 
 
-def time_graphs(torch, graphs, steps: int, warmup: int):
-    """Replays graphs[i % len] warmup times, then times exactly `steps` replays; ms per replay."""
+# Untimed replays before every timed figure. After an idle gap (a graph
+# capture, host work) the chip's power management slows VALU-heavy kernels
+# for roughly 3-30 ms of renewed load: the M = 2 head runs 91 us per launch in
+# its first ~30 launches, 110-128 us in the next ~150, and 91-92 us from ~400
+# on. Timing starts once the figure's own work has run for this long.
+SETTLE_S = 50e-3
+
+
+def time_graphs(torch, graphs, steps: int, warmup: int, settle_s: float = SETTLE_S):
+    """Replays graphs[i % len] for settle_s seconds and then warmup times,
+    untimed, then times exactly `steps` replays; ms per replay."""
+    t0, i = time.perf_counter(), 0
+    while True:
+        for _ in range(4):
+            graphs[i % len(graphs)].replay()
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= settle_s:
+            break
     for i in range(warmup):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()

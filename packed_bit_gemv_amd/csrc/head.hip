@@ -518,6 +518,129 @@ __global__ __launch_bounds__(kPWaves* kWave) void int8_head_persist_kernel(const
   }
 }
 
+// 3 <= M <= 4 with k % 1024 == 0, k <= 4096 and n >= 8 (w and x 16-byte
+// aligned), on the VALU. Persistent: a workgroup holds one wave per 1,024-column K-slice;
+// each wave keeps its slice of the M activation rows in registers for the
+// whole launch and walks row groups b, b + grid, ... of kXRows rows, with the
+// next group's loads (and the scale of the value each thread finishes) in
+// flight while the current group is converted, multiplied and reduced. The
+// slices meet in LDS in slice order, in a buffer that alternates between
+// groups, so one barrier per group suffices. With x read once per wave rather
+// than once per group, the M dot2 per weight pair and the conversion stay
+// within the issue budget of the 622 MB stream up to M = 4; at M = 3 and 4 this
+// measured 99.8-100.7 and 102.3-103.5 us against 107.8-109.6 us for the
+// persistent matrix-core kernel below, and slower from M = 5.
+constexpr int kXRows = 8;
+constexpr int kXSlice = 1024;
+
+template <int M, int SW, bool AM>
+__global__ __launch_bounds__(SW* kWave) void int8_head_xreg_kernel(const int8_t* __restrict__ w,
+                                                                    const float* __restrict__ scale, int64_t n,
+                                                                    const uint16_t* __restrict__ x,
+                                                                    float* __restrict__ y,
+                                                                    unsigned long long* __restrict__ keys) {
+  constexpr int kVals = kXRows * M;  // (row i, activation row m) at i * M + m
+  constexpr int kRed = (kVals + 3) / 4;
+  static_assert(kVals % 4 == 0 && kVals <= kWave, "the first wave finishes every value");
+  __shared__ float part[2][SW][4 * kRed];
+  __shared__ unsigned long long wg_key[AM ? M : 1];
+  if constexpr (AM) {
+    if (threadIdx.x < M) wg_key[threadIdx.x] = 0ull;  // ordered before use by the first group's barrier
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int slot = reduce4_slot(lane);
+  constexpr int64_t chunks = SW * kXSlice / 16, groups = SW * kXSlice / 8;  // k = SW * kXSlice
+  const int64_t c = static_cast<int64_t>(s) * kWave + lane;  // this lane's 16 weights of every row
+  const uint4* wq = reinterpret_cast<const uint4*>(w);
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+  uint32_t xp[M][8];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint4 a = xg[m * groups + 2 * c], b = xg[m * groups + 2 * c + 1];
+    xp[m][0] = a.x;
+    xp[m][1] = a.y;
+    xp[m][2] = a.z;
+    xp[m][3] = a.w;
+    xp[m][4] = b.x;
+    xp[m][5] = b.y;
+    xp[m][6] = b.z;
+    xp[m][7] = b.w;
+  }
+  const int64_t ng = (n + kXRows - 1) / kXRows;
+  const int64_t stride = gridDim.x;
+  const int ti = (threadIdx.x < kVals ? threadIdx.x : 0) / M;  // row of the value this thread finishes
+  // Group g covers rows g * kXRows .. + kXRows - 1; the last group is read as
+  // the final kXRows rows of the head (n >= kXRows), so no row needs a clamp,
+  // and it stores only the rows not stored by the group before it.
+  auto first_row = [&](int64_t g) {
+    const int64_t r0 = g * kXRows;
+    return r0 < n - kXRows ? r0 : n - kXRows;
+  };
+  auto load = [&](int64_t g, uint4 (&wv)[kXRows], float& scl) {
+    const int64_t rs = first_row(g < ng ? g : ng - 1);
+    const uint4* base = wq + rs * chunks + c;
+#pragma unroll
+    for (int i = 0; i < kXRows; ++i) wv[i] = load_nt(base + i * chunks);
+    scl = scale[rs + ti];
+  };
+  auto step = [&](int64_t g, const uint4 (&wv)[kXRows], int buf, float scl) {
+    float acc[kVals];
+#pragma unroll
+    for (int i = 0; i < kXRows; ++i) {
+      uint32_t hp[8];
+      int8x4_to_half2x2(wv[i].x, hp[0], hp[1]);
+      int8x4_to_half2x2(wv[i].y, hp[2], hp[3]);
+      int8x4_to_half2x2(wv[i].z, hp[4], hp[5]);
+      int8x4_to_half2x2(wv[i].w, hp[6], hp[7]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        // the first dot2 of the chain takes an inline zero (no zeroing move)
+        float a;
+        asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(a) : "v"(hp[0]), "v"(xp[m][0]));
+#pragma unroll
+        for (int p = 1; p < 8; ++p) a = dot2(hp[p], xp[m][p], a);
+        acc[i * M + m] = a;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kRed; ++q) {
+      const float red = wave_reduce4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      if (slot >= 0) part[buf][s][4 * q + slot] = red;
+    }
+    __syncthreads();
+    if (threadIdx.x < kVals) {
+      const int64_t r = first_row(g) + ti;
+      if (r >= g * kXRows) {
+        float sum = part[buf][0][threadIdx.x];
+#pragma unroll
+        for (int t = 1; t < SW; ++t) sum += part[buf][t][threadIdx.x];
+        const float v = sum * scl;
+        const int m = threadIdx.x % M;
+        if constexpr (AM) atomicMax(&wg_key[m], argmax_key(v, r));
+        else y[static_cast<int64_t>(m) * n + r] = v;
+      }
+    }
+  };
+  uint4 wa[kXRows], wb[kXRows];
+  float sa, sb;
+  int64_t g = blockIdx.x;
+  load(g, wa, sa);
+  for (; g < ng; g += 2 * stride) {  // workgroup-uniform
+    load(g + stride, wb, sb);
+    __builtin_amdgcn_sched_barrier(0);
+    step(g, wa, 0, sa);
+    if (g + stride >= ng) break;
+    load(g + 2 * stride, wa, sa);
+    __builtin_amdgcn_sched_barrier(0);
+    step(g + stride, wb, 1, sb);
+  }
+  if constexpr (AM) {
+    __syncthreads();
+    if (threadIdx.x < M) atomicMax(argmax_bin(keys, threadIdx.x), wg_key[threadIdx.x]);
+  }
+}
+
 // Compute units of the current device (queried once per device).
 int compute_units() {
   static std::atomic<int> cache[64];
@@ -545,26 +668,44 @@ void launch_head_persist(const int8_t* w, const float* scale, int64_t n, int64_t
 }
 
 template <int M, bool AM>
+void launch_head_xreg(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
+                      unsigned long long* keys, hipStream_t stream) {
+  // three workgroups per CU: 3-4 waves per SIMD at 120-140 VGPRs
+  const int64_t ng = (n + kXRows - 1) / kXRows;
+  const int64_t cap = 3 * static_cast<int64_t>(compute_units());
+  const dim3 grid(static_cast<unsigned>(ng < cap ? ng : cap));
+  switch (k / kXSlice) {  // the K-slices, one wave each, as a constant for the address arithmetic
+    case 1: hipLaunchKernelGGL((int8_head_xreg_kernel<M, 1, AM>), grid, dim3(kWave), 0, stream, w, scale, n, x, y, keys); break;
+    case 2: hipLaunchKernelGGL((int8_head_xreg_kernel<M, 2, AM>), grid, dim3(2 * kWave), 0, stream, w, scale, n, x, y, keys); break;
+    case 3: hipLaunchKernelGGL((int8_head_xreg_kernel<M, 3, AM>), grid, dim3(3 * kWave), 0, stream, w, scale, n, x, y, keys); break;
+    default: hipLaunchKernelGGL((int8_head_xreg_kernel<M, 4, AM>), grid, dim3(4 * kWave), 0, stream, w, scale, n, x, y, keys); break;
+  }
+}
+
+template <int M, bool AM>
 void launch_head_any(const int8_t* w, const float* scale, int64_t n, int64_t k, const uint16_t* x, float* y,
                      unsigned long long* keys, hipStream_t stream) {
   const bool aligned = k % 16 == 0 && (reinterpret_cast<uintptr_t>(w) & 15u) == 0 &&
                        (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   const int64_t units = (k / 16 + 3) / 4;  // 64-column units
   if (aligned && M == 1) {
-    // two groups of 8 rows per 8-wave workgroup. Two groups of 4 rows took
-    // 85.4-86.6 against 92.2-93.1 us when timed on their own, but inside the
-    // benchmark's sequence 93.9-100.5 against 90.8-91.5 us (greedy argmax:
-    // 106.5-107.7 against 95.6-97.5 us) with the decode step unchanged, so
-    // the 8-row groups stay.
-    launch_head_fast<1, 4, 2, 8, AM>(w, scale, n, k, x, y, keys, stream);
+    // two groups of 4 rows per 8-wave workgroup: 85.6-86.3 us at steady
+    // clocks against 92.1-93.0 for two groups of 8 rows and 86.9-90.2 for one
+    // group of 4 to 12 (graph-timed, bit-identical). Timed within ~30 ms of an
+    // idle gap, while power management holds the VALU-heavier launches back,
+    // the 4-row groups measured slower than the 8-row ones.
+    launch_head_fast<1, 4, 2, 4, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M == 2) {
     // two activation rows still fit the VALU path. One group of 8 rows per
     // 4-wave workgroup streams the 151,936 x 4,096 head at the rate of a
-    // plain read: 91.0 us, against 99.1-99.9 us for two groups of 4 rows and
-    // 106.8 us for the persistent matrix-core kernel (graph-timed sweep of
-    // six shapes). From M = 3 every VALU shape loses to the persistent kernel
-    // (best 111.8 against 108.4 us at M = 3, 120.8 against 109.8 at M = 4).
+    // plain read: 89.6-92.9 us at steady clocks, against 96.7-98.6 us for
+    // groups of 4 rows and 106.8 us for the persistent matrix-core kernel.
+    // Workgroups that re-read x for every group of rows lose from M = 3
+    // (best 111.8 against 108.4 us at M = 3); the kernel above, which keeps
+    // x in registers, takes M = 3 and 4.
     launch_head_fast<2, 4, 1, 8, AM>(w, scale, n, k, x, y, keys, stream);
+  } else if (aligned && (M == 3 || M == 4) && k % kXSlice == 0 && k <= 4 * kXSlice && n >= kXRows) {
+    if constexpr (M == 3 || M == 4) launch_head_xreg<M, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && k % kPKStep == 0 && k <= kPMaxK) {
     launch_head_persist<M, AM>(w, scale, n, k, x, y, keys, stream);
   } else if (aligned && M >= 3 && units <= 8 * 16) {

@@ -313,7 +313,7 @@ def test_small_m_config_shapes(pbg, m, proj):
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(1, 16), (3, 5), (17, 100), (40, 4096), (33, 4112), (9, 12288), (1000, 4096),
-                                 (40000, 1024), (4100, 2048), (33, 3072)])
+                                 (40000, 1024), (4100, 2048), (33, 3072), (5, 4096)])
 def test_head_exact_probe(pbg, m, n, k):
     say(f"head exact m={m} n={n} k={k}")
     w = synth.int8_full_range(10000 + n + k, n, k)
@@ -336,7 +336,7 @@ def test_head_random_tolerance(pbg, m):
     assert_within(y, ref, head_bound(w, s, x), f"head m={m}")
 
 
-@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("m", [1, 4, 8])
 def test_head_full_size_sampled(pbg, m):
     n, k = synth.HEAD_SHAPE
     say(f"head full-size sampled m={m}")
@@ -525,7 +525,7 @@ def test_head_argmax_random(pbg, m):
             assert t == tok_ref[i]
 
 
-@pytest.mark.parametrize("m", [1, 7])
+@pytest.mark.parametrize("m", [1, 3, 7])
 def test_head_argmax_full_size(pbg, m):
     n, k = synth.HEAD_SHAPE
     say(f"argmax full head m={m}")
