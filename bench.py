@@ -139,11 +139,12 @@ def capture(torch, fn):
 SETTLE_S = 50e-3
 
 
-def time_graphs(torch, graphs, steps: int, warmup: int, settle_s: float = SETTLE_S):
-    """Replays graphs[i % len] for settle_s seconds and then warmup times,
-    untimed, then times exactly `steps` replays; ms per replay."""
+def time_graphs(torch, graphs, steps: int, warmup: int, settle_s: float | None = None):
+    """Replays graphs[i % len] for settle_s seconds (SETTLE_S by default) and
+    then warmup times, untimed, then times exactly `steps` replays; ms per replay."""
+    settle_s = SETTLE_S if settle_s is None else settle_s
     t0, i = time.perf_counter(), 0
-    while True:
+    while settle_s > 0:
         for _ in range(4):
             graphs[i % len(graphs)].replay()
             i += 1
@@ -238,6 +239,7 @@ def cpu_baseline(budget_s: float):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -248,7 +250,11 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    # untimed replays before each extra figure (and the roofline launch); 0
+    # only for counter runs, whose bytes and instructions do not depend on clocks
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_S * 1e3)
     args = ap.parse_args()
+    SETTLE_S = args.settle_ms * 1e-3
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -733,6 +739,7 @@ def main():
             "bytes_per_step": bytes_step,
             "path": "ternary_ffn_swiglu: gate|up + SwiGLU in one launch, then the down GEMV on its fp16 output",
             "untimed": f"{settle_steps} settle steps (~20 ms, for the clocks) then the {args.warmup} warm-up steps",
+            "extra_settle_ms": args.settle_ms,
             "plain_three_gemv": {"us_per_step": round(three_us, 3),
                                  "GBs": round(three_bytes / (three_us * 1e-6) / 1e9, 1),
                                  "bytes_per_step": three_bytes},
@@ -753,7 +760,8 @@ def main():
             "read_ceiling_note": "pbg_stream_read of the launch's packed bytes (25,165,824 B): the GEMVs' loads "
                                  "alone, one launch each, timed the same way",
             "launch_us_note": f"HIP events around a replayed graph of {L} consecutive launches over the pool, "
-                              f"divided by {L} (inter-launch gaps included)",
+                              f"divided by {L} (inter-launch gaps included), after {args.settle_ms:g} ms of "
+                              f"untimed replays",
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
         "extra": extra,
